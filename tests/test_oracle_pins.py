@@ -1,0 +1,426 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test checks one oracle function against a library routine, a brute-force
+search, exact rational arithmetic, a hand-derived closed form or an invariant
+of the method, chosen so that a dropped term, a wrong sign or index, or a
+transposed operand fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_ffn_histogram_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+E2M1 = json.load(open(os.path.join(GOLDEN, "e2m1_values.json")))["values"]
+
+
+# --------------------------------------------------------------------------
+# codecs: exhaustive decodes against torch's format definitions
+# --------------------------------------------------------------------------
+def test_dec_e4m3_exhaustive_vs_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.dec_e4m3(b) for b in range(256)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+
+
+def test_dec_e8m0_exhaustive_vs_torch():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    got = np.array([oracle.dec_e8m0(b) for b in range(256)])
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(ref[:255], got[:255])
+
+
+def test_dec_e2m1_all_codes_vs_format_table():
+    got = [oracle.dec_e2m1(n) for n in range(16)]
+    assert got == E2M1
+    assert [math.copysign(1, v) for v in got] == [math.copysign(1, v) for v in E2M1]
+
+
+def test_dec_bf16_exhaustive_vs_torch():
+    bits = torch.arange(65536, dtype=torch.int32).to(torch.int16)
+    ref = bits.view(torch.bfloat16).double().numpy()
+    got = np.array([oracle.dec_bf16(b) for b in range(0, 65536, 7)])
+    r = ref[::7]
+    assert np.array_equal(np.isnan(r), np.isnan(got))
+    ok = ~np.isnan(r)
+    assert np.array_equal(r[ok], got[ok])
+
+
+# --------------------------------------------------------------------------
+# element rounding: brute-force nearest search and torch's casts
+# --------------------------------------------------------------------------
+def _e4m3_finite_table():
+    vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    codes = np.arange(256)
+    ok = ~np.isnan(vals)
+    return vals[ok], codes[ok]
+
+
+def _brute_e4m3(v, vals, codes):
+    """Nearest finite e4m3 value; ties to the code with even mantissa bit; saturating."""
+    d = np.abs(vals - v)
+    best = d.min()
+    cand = np.where(d == best)[0]
+    if len(cand) > 1:
+        even = [c for c in cand if codes[c] % 2 == 0 and vals[c] != 0 or vals[c] == 0]
+        cand = even if even else cand
+    return vals[cand[0]]
+
+
+def test_round_e4m3_bruteforce_sweep():
+    vals, codes = _e4m3_finite_table()
+    rng = np.random.default_rng(0)
+    pos = np.unique(np.abs(vals))
+    mids = (pos[1:] + pos[:-1]) / 2                      # exact ties
+    pts = np.concatenate([vals, mids, -mids, rng.uniform(-500, 500, 3000),
+                          rng.standard_normal(2000) * 2.0 ** rng.integers(-12, 9, 2000),
+                          [449.0, 460.0, 464.0, 500.0, -470.0, 1e-9, -1e-9, 2.0 ** -10, 3 * 2.0 ** -11]])
+    for v in pts:
+        got = oracle.round_e4m3_sat(v)
+        exp = _brute_e4m3(v, vals, codes)
+        assert got == exp, (v, got, exp)
+
+
+def test_round_e4m3_matches_torch_cast_in_range():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 3]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).double().numpy()
+    got = np.array([oracle.round_e4m3_sat(float(a)) for a in v])
+    assert np.array_equal(ref, got)
+
+
+def test_enc_e4m3_roundtrip_all_finite_codes():
+    for b in range(256):
+        v = oracle.dec_e4m3(b)
+        if math.isnan(v):
+            continue
+        assert oracle.enc_e4m3(v) == b, b
+
+
+def test_round_bf16_matches_torch_cast():
+    rng = np.random.default_rng(2)
+    v = np.concatenate([rng.standard_normal(20000) * 2.0 ** rng.integers(-30, 30, 20000),
+                        # exact ties between neighbouring bf16 values
+                        ((rng.integers(1 << 14, 1 << 15, 3000) * 2 + 1) * 2.0 ** -16)]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+    got = np.array([oracle.round_bf16(float(a)) for a in v])
+    assert np.array_equal(ref, got)
+    enc = np.array([oracle.enc_bf16(g) for g in got], dtype=np.uint16)
+    assert np.array_equal(enc, torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# scale rule: the defining inequalities (no clipping, and minimal)
+# --------------------------------------------------------------------------
+def test_scale_exp_is_smallest_nonclipping_power():
+    rng = np.random.default_rng(3)
+    amaxes = np.concatenate([rng.uniform(0, 1, 500) * 2.0 ** rng.integers(-40, 40, 500),
+                             [448.0 * 2.0 ** n for n in range(-20, 20)],
+                             [np.nextafter(448.0 * 2.0 ** n, 0) for n in range(-5, 5)],
+                             [np.nextafter(448.0 * 2.0 ** n, np.inf) for n in range(-5, 5)]])
+    for a in amaxes:
+        E = oracle.scale_exp(a)
+        assert a <= 448.0 * 2.0 ** E, a
+        assert a > 448.0 * 2.0 ** (E - 1), a
+    assert oracle.scale_exp(0.0) == 0
+    assert oracle.scale_exp(448.0) == 0
+    assert oracle.scale_exp(1e-300) == -127          # clamped
+    assert oracle.scale_exp(1e300) == 127            # clamped
+
+
+# --------------------------------------------------------------------------
+# activation: torch's silu in float64, closed points, clamp of both inputs
+# --------------------------------------------------------------------------
+def test_swiglu_vs_torch_silu():
+    rng = np.random.default_rng(4)
+    g = (rng.standard_normal(3000) * 4).astype(np.float32)
+    u = (rng.standard_normal(3000) * 4).astype(np.float32)
+    ref = (torch.nn.functional.silu(torch.from_numpy(g).double()) * torch.from_numpy(u).double()).float().numpy()
+    got = np.array([oracle.swiglu(a, b, 0.0) for a, b in zip(g, u)], dtype=np.float32)
+    assert np.max(np.abs(got - ref) / (np.abs(ref) + 1e-30)) < 2e-7
+
+
+def test_swiglu_closed_points_and_clamp():
+    silu = lambda v: float(torch.nn.functional.silu(torch.tensor(v, dtype=torch.float64)))
+    assert oracle.swiglu(0.0, 5.0, 7.0) == 0.0
+    assert oracle.swiglu(3.0, 0.0, 7.0) == 0.0
+    assert oracle.swiglu(100.0, 2.0, 7.0) == np.float32(silu(7.0) * 2.0)
+    assert oracle.swiglu(-100.0, 2.0, 7.0) == np.float32(silu(-7.0) * 2.0)
+    assert oracle.swiglu(1.5, 100.0, 7.0) == np.float32(silu(1.5) * 7.0)
+    assert oracle.swiglu(1.5, -100.0, 7.0) == np.float32(silu(1.5) * -7.0)
+    for off in (0.0, -1.0, float("inf"), float("nan")):
+        assert oracle.swiglu(100.0, 2.0, off) == np.float32(silu(100.0) * 2.0)
+    # gate and up are not interchangeable
+    assert oracle.swiglu(2.0, -3.0, 0.0) != oracle.swiglu(-3.0, 2.0, 0.0)
+
+
+# --------------------------------------------------------------------------
+# routing: brute-force sort and invariants
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("T,k,E", [(0, 2, 4), (1, 1, 1), (7, 3, 5), (64, 8, 16), (300, 6, 64)])
+def test_route_vs_bruteforce_sort(T, k, E):
+    rng = np.random.default_rng(T * 31 + E)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    if T:
+        idx[rng.random((T, k)) < 0.15] = -1
+    counts, offsets, r2s, s2r, rc = oracle.route(idx, E)
+    flat = idx.ravel()
+    valid = [s for s in range(T * k) if 0 <= flat[s] < E]
+    order = sorted(valid, key=lambda s: (flat[s], s))
+    assert rc == oracle.OK
+    assert r2s.tolist() == order
+    assert counts.tolist() == [int((flat == e).sum()) for e in range(E)]
+    assert offsets[0] == 0 and np.all(np.diff(offsets) == counts) and offsets[-1] == len(valid)
+    for r, s in enumerate(r2s):
+        assert s2r[s] == r
+    assert all(s2r[s] == -1 for s in range(T * k) if flat[s] == -1)
+
+
+def test_route_bad_index_is_masked_and_reported():
+    idx = np.array([[0, 5], [-1, 1], [-3, 2]], np.int32)
+    counts, offsets, r2s, s2r, rc = oracle.route(idx, 4)
+    assert rc == oracle.BAD_EXPERT_INDEX
+    assert counts.tolist() == [1, 1, 1, 0]
+    assert s2r.tolist() == [0, -1, -1, 1, -1, 2]
+
+
+# --------------------------------------------------------------------------
+# GEMMs: exact rational arithmetic on tiny shapes
+# --------------------------------------------------------------------------
+def _torch_dequant_act(p, t):
+    H = p["H"]
+    if p["recipe"] == synth.RECIPE_BF16:
+        return [Fraction(float(v)) for v in torch.from_numpy(p["x"][t].view(np.int16)).view(torch.bfloat16).double()]
+    vals = torch.from_numpy(p["x"][t]).view(torch.float8_e4m3fn).double().numpy()
+    sc = torch.from_numpy(p["x_sf"][t]).view(torch.float8_e8m0fnu).double().numpy()
+    return [Fraction(float(vals[h])) * Fraction(float(sc[h // 32])) for h in range(H)]
+
+
+def _torch_dequant_w(p, which, e, n):
+    w, sf = p[which], p[which + "_sf"]
+    if p["recipe"] == synth.RECIPE_BF16:
+        return [Fraction(float(v)) for v in torch.from_numpy(w[e, n].view(np.int16)).view(torch.bfloat16).double()]
+    sc = torch.from_numpy(sf[e, n]).view(torch.float8_e8m0fnu).double().numpy()
+    if p["recipe"] == synth.RECIPE_FP8_FP8:
+        vals = torch.from_numpy(w[e, n]).view(torch.float8_e4m3fn).double().numpy()
+    else:
+        b = w[e, n]
+        vals = np.empty(2 * len(b))
+        vals[0::2] = [E2M1[v & 15] for v in b]
+        vals[1::2] = [E2M1[v >> 4] for v in b]
+    return [Fraction(float(vals[kk])) * Fraction(float(sc[kk // 32])) for kk in range(len(vals))]
+
+
+@pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4])
+def test_gemms_exact_rationals(recipe):
+    cfg = synth.Config("tiny", recipe, 3, 64, 32, 3, 2, "uniform", 11)
+    p = synth.make_problem(cfg, threads=1)
+    t, e = 1, int(p["topk_idx"][1, 0])
+    row = oracle.ffn_row(p, t, e, 7.0)
+    xq = _torch_dequant_act(p, t)
+    for n in range(2 * p["I"]):
+        wq = _torch_dequant_w(p, "w1", e, n)
+        exact = sum(a * b for a, b in zip(xq, wq))
+        assert np.float32(float(exact)) == row["c"][n], n   # one rounding of the exact sum
+    hq = [Fraction(float(v)) for v in row["hq"]]
+    for n in range(p["H"]):
+        wq = _torch_dequant_w(p, "w2", e, n)
+        exact = sum(a * b for a, b in zip(hq, wq))
+        assert np.float32(float(exact)) == row["o"][n], n
+
+
+def test_requant_row_codes_decode_to_hq_and_obey_scale_rule():
+    cfg = synth.CONFIGS["fp8xfp8_T512_H2048_I768_E64_k6"].with_(T=4)
+    p = synth.make_problem(cfg.with_(E=4, H=256, I=128), threads=1)
+    row = oracle.ffn_row(p, 2, 1, 7.0)
+    codes = torch.from_numpy(row["h_codes"]).view(torch.float8_e4m3fn).double().numpy()
+    sc = torch.from_numpy(row["h_sf"]).view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(codes * np.repeat(sc, 32), row["hq"])
+    h = row["h"].astype(np.float64)
+    for b in range(len(sc)):
+        blk = np.abs(h[32 * b:32 * b + 32])
+        q = np.abs(codes[32 * b:32 * b + 32])
+        assert q.max() <= 448.0
+        if blk.max() > 0:
+            assert q.max() >= 224.0          # minimal scale: amax * 2^-E > 224, which rounds to >= 224
+            # torch's cast of h * 2^-E reproduces the codes (E from the byte)
+            t = torch.from_numpy((h[32 * b:32 * b + 32] / sc[b]).astype(np.float32)).to(torch.float8_e4m3fn)
+            assert np.array_equal(t.view(torch.uint8).numpy(), row["h_codes"][32 * b:32 * b + 32])
+
+
+# --------------------------------------------------------------------------
+# whole forward: hand-derived closed form
+# --------------------------------------------------------------------------
+def _closed_form_problem():
+    T, H, I, E, k = 2, 32, 32, 2, 2
+    p = {"name": "closed", "T": T, "H": H, "I": I, "E": E, "k": k, "recipe": synth.RECIPE_FP8_FP4}
+    p["x"] = np.full((T, H), 0x38, np.uint8)
+    p["x_sf"] = np.full((T, H // 32), 127, np.uint8)
+    w1 = np.zeros((E, 2 * I, H // 2), np.uint8)
+    w1[:, :I] = 0x11      # E2M1 0.5 in both nibbles
+    w1[:, I:] = 0xAA      # E2M1 -1.0 in both nibbles
+    p["w1"], p["w1_sf"] = w1, np.full((E, 2 * I, H // 32), 127, np.uint8)
+    w2 = np.zeros((E, H, I // 2), np.uint8)
+    w2[0] = 0x22          # 1.0
+    w2[1] = 0x44          # 2.0
+    p["w2"], p["w2_sf"] = w2, np.full((E, H, I // 32), 127, np.uint8)
+    p["topk_idx"] = np.array([[1, -1], [0, 1]], np.int32)
+    p["topk_weights"] = np.array([[1.0, 0.5], [0.25, 0.75]], np.float32)
+    return p
+
+
+@pytest.mark.parametrize("case,clamp", [("clamp7", 7.0), ("no_clamp", 0.0)])
+def test_closed_form_example(case, clamp):
+    gold = json.load(open(os.path.join(GOLDEN, "closed_form_example.json")))["expected"][case]
+    p = _closed_form_problem()
+    out = oracle.forward(p, y_fp32=True, clamp=clamp)
+    assert np.all(out["y"][0] == gold["y"][0]) and np.all(out["y"][1] == gold["y"][1])
+    row = oracle.ffn_row(p, 1, 0, clamp)
+    assert np.all(row["h_sf"] == gold["h_sf_byte"])
+    assert np.all(row["h_codes"] == gold["h_code"])
+    assert np.all(row["hq"] == gold["h_value"])
+    yb = oracle.forward(p, y_fp32=False, clamp=clamp)["y"]
+    assert np.array_equal(oracle.bf16_bits_to_f32(yb), out["y"])   # these values are bf16-exact
+
+
+# --------------------------------------------------------------------------
+# whole forward: dense special case through library routines
+# --------------------------------------------------------------------------
+def _identical_experts(p):
+    q = dict(p)
+    for n in ("w1", "w1_sf", "w2", "w2_sf"):
+        if p[n] is not None:
+            q[n] = np.ascontiguousarray(np.broadcast_to(p[n][:1], p[n].shape))
+    return q
+
+
+def _dense_ffn_torch(p, t, clamp):
+    """One dense SwiGLU FFN (expert 0) on token t with torch float64 linear algebra and torch casts."""
+    x = torch.tensor([float(v) for v in _torch_dequant_act(p, t)], dtype=torch.float64)
+    W1 = torch.tensor([[float(v) for v in _torch_dequant_w(p, "w1", 0, n)] for n in range(2 * p["I"])],
+                      dtype=torch.float64)
+    W2 = torch.tensor([[float(v) for v in _torch_dequant_w(p, "w2", 0, n)] for n in range(p["H"])],
+                      dtype=torch.float64)
+    c = torch.nn.functional.linear(x, W1).float().double()
+    g, u = c[: p["I"]], c[p["I"]:]
+    if clamp > 0:
+        g, u = g.clamp(-clamp, clamp), u.clamp(-clamp, clamp)
+    h = (torch.nn.functional.silu(g) * u).float()
+    if p["recipe"] == synth.RECIPE_BF16:
+        hq = h.to(torch.bfloat16).double()
+    else:
+        hq = torch.empty_like(h, dtype=torch.float64)
+        for b in range(p["I"] // 32):
+            blk = h[32 * b:32 * b + 32].double()
+            amax = float(blk.abs().max())
+            E = 0
+            if amax > 0:   # brute-force search for the smallest non-clipping power of two
+                E = -127
+                while 448.0 * 2.0 ** E < amax:
+                    E += 1
+            hq[32 * b:32 * b + 32] = (blk * 2.0 ** -E).float().to(torch.float8_e4m3fn).double() * 2.0 ** E
+    return torch.nn.functional.linear(hq, W2).float()
+
+
+@pytest.mark.parametrize("recipe,k,w", [(synth.RECIPE_FP8_FP4, 2, (0.25, 0.75)),
+                                        (synth.RECIPE_FP8_FP8, 8, (0.125,) * 8),
+                                        (synth.RECIPE_BF16, 2, (0.5, 0.5))])
+def test_identical_experts_reduce_to_dense_ffn(recipe, k, w):
+    cfg = synth.Config("dense", recipe, 3, 64, 64, 4 if k == 2 else 9, k, "uniform", 21)
+    p = _identical_experts(synth.make_problem(cfg, threads=1))
+    p["topk_weights"] = np.tile(np.array(w, np.float32), (p["T"], 1))
+    for clamp in (7.0, 0.0):
+        out = oracle.forward(p, y_fp32=True, clamp=clamp)
+        outb = oracle.forward(p, y_fp32=False, clamp=clamp)
+        for t in range(p["T"]):
+            ref = _dense_ffn_torch(p, t, clamp).numpy()
+            assert np.array_equal(out["y"][t], ref), t
+            refb = torch.from_numpy(ref).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+            assert np.array_equal(outb["y"][t], refb), t
+
+
+# --------------------------------------------------------------------------
+# whole forward: invariants
+# --------------------------------------------------------------------------
+def _small(recipe, routing="softmax", T=24, seed=5):
+    cfg = synth.Config("small", recipe, T, 64, 64, 6, 3, routing, seed)
+    return synth.make_problem(cfg, threads=1)
+
+
+@pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4])
+def test_empty_experts_contribute_nothing(recipe):
+    p = _small(recipe)
+    used = set(p["topk_idx"].ravel().tolist())
+    p["topk_idx"][p["topk_idx"] == 5] = 4          # make sure expert 5 is unused
+    used = set(p["topk_idx"].ravel().tolist())
+    ref = oracle.forward(p, True, 7.0)["y"]
+    q = dict(p)
+    for n in ("w1", "w2"):
+        a = p[n].copy()
+        for e in range(p["E"]):
+            if e not in used:
+                a[e] = 0x7F if recipe != synth.RECIPE_BF16 else 0x7FC0   # e4m3 NaN / bf16 NaN
+        q[n] = a
+        if p[n + "_sf"] is not None:
+            s = p[n + "_sf"].copy()
+            for e in range(p["E"]):
+                if e not in used:
+                    s[e] = 0xFF                                           # e8m0 NaN
+            q[n + "_sf"] = s
+    got = oracle.forward(q, True, 7.0)["y"]
+    assert np.all(np.isfinite(got)) and np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("recipe", [synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4])
+def test_token_permutation_permutes_output(recipe):
+    p = _small(recipe)
+    perm = np.random.default_rng(9).permutation(p["T"])
+    q = dict(p)
+    for n in ("x", "x_sf", "topk_idx", "topk_weights"):
+        q[n] = np.ascontiguousarray(p[n][perm])
+    a = oracle.forward(p, False, 7.0)["y"]
+    b = oracle.forward(q, False, 7.0)["y"]
+    assert np.array_equal(a[perm], b)
+
+
+@pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP4])
+def test_per_token_path_equals_routed_path(recipe):
+    p = _small(recipe, T=20)
+    p["topk_idx"][3, 1] = -1
+    full = oracle.forward(p, False, 7.0)["y"]
+    toks = [19, 0, 3, 7]
+    y, rc = oracle.forward_tokens(p, toks, False, 7.0)
+    assert rc == oracle.OK
+    assert np.array_equal(full[toks], y)
+
+
+def test_masking_equals_zero_weight_and_weights_are_linear():
+    p = _small(synth.RECIPE_FP8_FP4)
+    q = dict(p, topk_idx=p["topk_idx"].copy(), topk_weights=p["topk_weights"].copy())
+    q["topk_idx"][::2, 0] = -1
+    r = dict(p, topk_weights=p["topk_weights"].copy())
+    r["topk_weights"][::2, 0] = 0.0
+    assert np.array_equal(oracle.forward(q, True, 7.0)["y"], oracle.forward(r, True, 7.0)["y"])
+    d = dict(p, topk_weights=p["topk_weights"] * 2)
+    assert np.array_equal(oracle.forward(d, True, 7.0)["y"], 2 * oracle.forward(p, True, 7.0)["y"])
+
+
+def test_token_without_valid_slot_is_zero_and_t0_is_noop():
+    p = _small(synth.RECIPE_FP8_FP8)
+    p["topk_idx"][5] = -1
+    y = oracle.forward(p, True, 7.0)["y"]
+    assert np.all(y[5] == 0.0)
+    q = dict(p, T=0, x=p["x"][:0].copy(), x_sf=p["x_sf"][:0].copy(),
+             topk_idx=p["topk_idx"][:0].copy(), topk_weights=p["topk_weights"][:0].copy())
+    out = oracle.forward(q, True, 7.0, want_tables=True)
+    assert out["y"].shape == (0, p["H"]) and out["counts"].sum() == 0
