@@ -1,0 +1,143 @@
+/*
+ * moe_ffn.h -- C ABI of the MI355X (gfx950) fused MoE expert-FFN forward.
+ *
+ * One call computes, for a batch of tokens already routed to their top-k
+ * experts, the "MegaMoE" forward described by the DeepGEMM / sglang pages:
+ *   1. routing: per-expert token histogram, exclusive prefix sum and a
+ *      stable (ascending slot) index scatter ("SM90 MegaMoE dev log",
+ *      Phase-2 entry: expert count, source token / top-k index write);
+ *   2. L1 grouped GEMM, hidden -> 2 x intermediate (gate rows, then up rows);
+ *   3. SwiGLU with activation clamp, re-quantised per 1x32 block
+ *      ("[Blackwell] Reserve SMs for DeepGEMM MegaMoE grid barriers" digest,
+ *      key-code section: activation="swiglu", activation_clamp, recipe
+ *      (1, 1, 32); dev log Phase-1 entry: l2_acts / l2_acts_sf views);
+ *   4. L2 grouped GEMM, intermediate -> hidden;
+ *   5. top-k weighted combine into y, deterministic (fixed slot order).
+ * The whole call is one persistent kernel whose grid is the CU count minus a
+ * tunable reserve, kept even ("[Blackwell] Reserve SMs ..." page, Summary /
+ * Fix / root cause; digest, implementation breakdown items 2-3), and which
+ * resets its own workspace counters on every call so that graph replay with
+ * changed inputs never consumes stale state ("[Bugfix] Reset MegaMoE combine
+ * readiness for CUDA graph replay", description).
+ *
+ * Conventions
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library never allocates, frees, memsets or synchronises.
+ *   - Row-major, last dimension contiguous, 16-byte aligned base pointers.
+ *   - e4m3 = OCP FP8 E4M3FN; e2m1 = OCP FP4 (two per byte, element 2j in the
+ *     low nibble, 2j+1 in the high nibble); e8m0 = power-of-two scale byte
+ *     2^(b-127) applying to one 1x32 block along the contraction dimension.
+ *   - Errors: functions return 0 (MOE_FFN_OK) or a negative MOE_FFN_ERR_*
+ *     code and never throw.  Device-side conditions are written to the
+ *     optional device int *status (MOE_FFN_STATUS_*).
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element recipe (the pages' recipe argument): */
+#define MOE_FFN_RECIPE_BF16 0     /* x, W1, W2 bf16; no scales; h re-rounded to bf16       */
+#define MOE_FFN_RECIPE_FP8_FP8 1  /* x, W e4m3 + e8m0 per 1x32 along K; h e4m3 + e8m0     */
+#define MOE_FFN_RECIPE_FP8_FP4 2  /* x e4m3, W e2m1 (packed), e8m0 per 1x32 along K       */
+
+/* Output element type of y. */
+#define MOE_FFN_Y_BF16 0
+#define MOE_FFN_Y_FP32 1
+
+/* Synchronous return codes. */
+#define MOE_FFN_OK 0
+#define MOE_FFN_ERR_INVALID_ARG (-1)        /* null pointer, negative size, misaligned pointer  */
+#define MOE_FFN_ERR_UNSUPPORTED (-2)        /* shape outside what the kernels handle            */
+#define MOE_FFN_ERR_WORKSPACE_TOO_SMALL (-3)
+#define MOE_FFN_ERR_HIP (-4)                /* a HIP runtime call failed (launch, device query) */
+
+/* Device status codes written to args.status (0 = success). */
+#define MOE_FFN_STATUS_OK 0
+#define MOE_FFN_STATUS_BAD_EXPERT_INDEX 1   /* an index outside [-1, E) was masked (y still valid) */
+#define MOE_FFN_STATUS_TIMEOUT 2            /* a grid barrier / readiness wait exceeded its bound; */
+                                            /* y is undefined; the workspace is left clean         */
+#define MOE_FFN_STATUS_DIRTY_WORKSPACE 3    /* counters were non-zero at entry; zero the workspace */
+
+/* Problem: fixes the workspace size and layout.  It does not depend on the
+   CU count or the reserve (digest: buffer cache key excludes the SM count). */
+typedef struct {
+    int64_t max_tokens;   /* capacity of x / y / topk rows (>= num_tokens of any call)         */
+    int64_t hidden;       /* H: multiple of 128 (64 for BF16)                                  */
+    int64_t intermediate; /* I: multiple of 128 (64 for BF16)                                  */
+    int64_t num_experts;  /* E: 1..512                                                         */
+    int64_t top_k;        /* k: 1..64                                                          */
+    int32_t recipe;       /* MOE_FFN_RECIPE_*                                                  */
+    int32_t reserved_;    /* must be 0                                                         */
+} moe_ffn_problem;
+
+/* Per-call arguments.  Shapes use T = num_tokens. */
+typedef struct {
+    int64_t num_tokens;          /* 0 <= T <= max_tokens; T = 0 writes no row of y                 */
+    const void* x;               /* [T, H] e4m3 bytes, or bf16 for the BF16 recipe                  */
+    const uint8_t* x_sf;         /* [T, H/32] e8m0; NULL for BF16                                   */
+    const int32_t* topk_idx;     /* [T, k] expert ids; -1 masks a slot                              */
+    const float* topk_weights;   /* [T, k] combine weights                                          */
+    const void* w1;              /* [E, 2I, H] (e2m1: [E, 2I, H/2] bytes); rows [0,I) gate, [I,2I) up */
+    const uint8_t* w1_sf;        /* [E, 2I, H/32] e8m0; NULL for BF16                               */
+    const void* w2;              /* [E, H, I] (e2m1: [E, H, I/2] bytes)                             */
+    const uint8_t* w2_sf;        /* [E, H, I/32] e8m0; NULL for BF16                                */
+    void* y;                     /* [T, H] of y_dtype; rows >= T untouched                          */
+    int32_t y_dtype;             /* MOE_FFN_Y_*                                                      */
+    float activation_clamp;      /* finite and > 0: clamp gate and up to [-c, c]; else no clamp      */
+    int32_t reserved_cus;        /* CUs left free for other streams; < 0: env MOE_FFN_RESERVED_CUS   */
+                                 /* or 2; the grid is even(min(cap, max(2, CUs - reserve)))          */
+    int32_t max_cus;             /* cap on the grid (0 = none)                                       */
+    int32_t* expert_counts;      /* optional [E] device out: rows per expert                         */
+    int32_t* expert_offsets;     /* optional [E+1] device out: exclusive prefix of counts            */
+    int32_t* row_to_slot;        /* optional [T*k] device out: first R = offsets[E] entries written  */
+    int32_t* slot_to_row;        /* optional [T*k] device out: row of each slot, -1 when masked      */
+    int32_t* status;             /* optional device int: MOE_FFN_STATUS_* of this call               */
+} moe_ffn_args;
+
+/* Bytes of device workspace one in-flight call needs (buffer-size query of the
+   dev log's Phase-1 host API).  The workspace must be zero-filled once after
+   allocation; afterwards every call leaves its counters zeroed.  One
+   workspace serves one call at a time: calls that overlap on it race. */
+int moe_ffn_get_workspace_size(const moe_ffn_problem* problem, size_t* bytes);
+
+/* Multiple that max_tokens must be a multiple of (token-alignment query of the
+   dev log's Phase-1 host API).  The kernels handle ragged expert groups, so
+   this is 1 for every recipe. */
+int moe_ffn_get_token_alignment(int32_t recipe, int64_t* alignment);
+
+/* Enqueue the forward on `stream` (a hipStream_t; NULL = default stream).
+   Asynchronous: returns after the launch; never synchronises, allocates or
+   memsets, so it can be captured into a HIP graph.  Thread-safe (no mutable
+   global state). */
+int moe_ffn_forward(const moe_ffn_problem* problem, const moe_ffn_args* args,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Text of a return or status code (static string). */
+const char* moe_ffn_strerror(int code);
+
+/* Host-only launch-size rule used by moe_ffn_forward: physical CUs minus the
+   reserve (negative reserve = 0), at least 2, capped by max_cus when > 0,
+   rounded down to even, at least 2 ("[Blackwell] Reserve SMs ..." digest,
+   implementation breakdown items 2-3). */
+int moe_ffn_launch_size(int physical_cus, int reserved_cus, int max_cus);
+
+/* Byte offsets of the intermediates inside the workspace, for inspection:
+   h ([max_tokens*k + pad, I] e4m3, or bf16), h_sf ([.., I/32] e8m0) and
+   o ([max_tokens*k, H] fp32 per routed row). */
+typedef struct {
+    size_t h, h_sf, o;
+    int64_t h_row_bytes, h_sf_row_bytes, o_row_bytes;
+} moe_ffn_workspace_view;
+int moe_ffn_get_workspace_view(const moe_ffn_problem* problem, moe_ffn_workspace_view* view);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FFN_H */

@@ -1,0 +1,174 @@
+"""MI355X (gfx950) fused MoE expert-FFN forward: Python binding of libmoe_ffn.so.
+
+The names mirror the C ABI in ``include/moe_ffn.h``; every function only
+marshals arguments (torch tensors -> device pointers) and calls the library.
+There is no CPU or PyTorch fallback: if the HIP library is missing, loading
+it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
+
+RECIPE_BF16 = 0
+RECIPE_FP8_FP8 = 1
+RECIPE_FP8_FP4 = 2
+Y_BF16 = 0
+Y_FP32 = 1
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_UNSUPPORTED = -2
+ERR_WORKSPACE_TOO_SMALL = -3
+ERR_HIP = -4
+STATUS_OK = 0
+STATUS_BAD_EXPERT_INDEX = 1
+STATUS_TIMEOUT = 2
+STATUS_DIRTY_WORKSPACE = 3
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("max_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
+                ("intermediate", ctypes.c_int64), ("num_experts", ctypes.c_int64),
+                ("top_k", ctypes.c_int64), ("recipe", ctypes.c_int32), ("reserved_", ctypes.c_int32)]
+
+
+class Args(ctypes.Structure):
+    _fields_ = [("num_tokens", ctypes.c_int64),
+                ("x", ctypes.c_void_p), ("x_sf", ctypes.c_void_p),
+                ("topk_idx", ctypes.c_void_p), ("topk_weights", ctypes.c_void_p),
+                ("w1", ctypes.c_void_p), ("w1_sf", ctypes.c_void_p),
+                ("w2", ctypes.c_void_p), ("w2_sf", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("y_dtype", ctypes.c_int32),
+                ("activation_clamp", ctypes.c_float),
+                ("reserved_cus", ctypes.c_int32), ("max_cus", ctypes.c_int32),
+                ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
+                ("row_to_slot", ctypes.c_void_p), ("slot_to_row", ctypes.c_void_p),
+                ("status", ctypes.c_void_p)]
+
+
+class WorkspaceView(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_size_t), ("h_sf", ctypes.c_size_t), ("o", ctypes.c_size_t),
+                ("h_row_bytes", ctypes.c_int64), ("h_sf_row_bytes", ctypes.c_int64),
+                ("o_row_bytes", ctypes.c_int64)]
+
+
+EXPORTS = ("moe_ffn_get_workspace_size", "moe_ffn_get_token_alignment", "moe_ffn_forward",
+           "moe_ffn_strerror", "moe_ffn_launch_size", "moe_ffn_get_workspace_view")
+
+_lib = None
+
+
+def lib():
+    """Load libmoe_ffn.so (raises OSError when it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"{LIB_PATH} is missing: build it with mixture_experts_ffn_histogram_amd/build.py "
+                          "(the forward has no fallback path)")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        L.moe_ffn_get_workspace_size.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_ffn_get_workspace_size.restype = ctypes.c_int
+        L.moe_ffn_get_token_alignment.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
+        L.moe_ffn_get_token_alignment.restype = ctypes.c_int
+        L.moe_ffn_forward.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Args), P, ctypes.c_size_t, P]
+        L.moe_ffn_forward.restype = ctypes.c_int
+        L.moe_ffn_strerror.argtypes = [ctypes.c_int]
+        L.moe_ffn_strerror.restype = ctypes.c_char_p
+        L.moe_ffn_launch_size.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        L.moe_ffn_launch_size.restype = ctypes.c_int
+        L.moe_ffn_get_workspace_view.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(WorkspaceView)]
+        L.moe_ffn_get_workspace_view.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+class MoeFFNError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+def _check(code: int, what: str) -> int:
+    if code != OK:
+        raise MoeFFNError(code, what)
+    return code
+
+
+def make_problem(max_tokens: int, hidden: int, intermediate: int, num_experts: int, top_k: int,
+                 recipe: int) -> Problem:
+    return Problem(int(max_tokens), int(hidden), int(intermediate), int(num_experts), int(top_k), int(recipe), 0)
+
+
+def get_workspace_size(problem: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().moe_ffn_get_workspace_size(ctypes.byref(problem), ctypes.byref(n)), "moe_ffn_get_workspace_size")
+    return int(n.value)
+
+
+def get_token_alignment(recipe: int) -> int:
+    a = ctypes.c_int64(0)
+    _check(lib().moe_ffn_get_token_alignment(int(recipe), ctypes.byref(a)), "moe_ffn_get_token_alignment")
+    return int(a.value)
+
+
+def get_workspace_view(problem: Problem) -> WorkspaceView:
+    v = WorkspaceView()
+    _check(lib().moe_ffn_get_workspace_view(ctypes.byref(problem), ctypes.byref(v)), "moe_ffn_get_workspace_view")
+    return v
+
+
+def strerror(code: int) -> str:
+    return lib().moe_ffn_strerror(int(code)).decode()
+
+
+def launch_size(physical_cus: int, reserved_cus: int, max_cus: int = 0) -> int:
+    return int(lib().moe_ffn_launch_size(int(physical_cus), int(reserved_cus), int(max_cus)))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, topk_weights,
+            w1, w1_sf, w2, w2_sf, y, y_dtype: int, activation_clamp: float,
+            reserved_cus: int = -1, max_cus: int = 0, expert_counts=None, expert_offsets=None,
+            row_to_slot=None, slot_to_row=None, status=None, stream=None) -> None:
+    """Enqueue moe_ffn_forward on `stream` (default: torch's current stream).
+
+    All tensors are device tensors laid out as include/moe_ffn.h states; the
+    workspace is a uint8 device tensor of at least get_workspace_size() bytes,
+    zero-filled once after allocation.
+    """
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    a = Args(int(num_tokens), _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),
+             _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf), _ptr(y), int(y_dtype), float(activation_clamp),
+             int(reserved_cus), int(max_cus), _ptr(expert_counts), _ptr(expert_offsets),
+             _ptr(row_to_slot), _ptr(slot_to_row), _ptr(status))
+    rc = lib().moe_ffn_forward(ctypes.byref(problem), ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
+                               ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                               ctypes.c_void_p(stream.cuda_stream))
+    _check(rc, "moe_ffn_forward")
+
+
+class MoeFFN:
+    """Owns a problem description and its zero-initialised workspace."""
+
+    def __init__(self, max_tokens, hidden, intermediate, num_experts, top_k, recipe, device="cuda"):
+        import torch
+        self.problem = make_problem(max_tokens, hidden, intermediate, num_experts, top_k, recipe)
+        self.workspace_bytes = get_workspace_size(self.problem)
+        self.workspace = torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=device)
+        self.recipe = recipe
+
+    def __call__(self, **kw) -> None:
+        forward(self.problem, self.workspace, **kw)
+
+    def view(self):
+        return get_workspace_view(self.problem)

@@ -1,0 +1,199 @@
+// Host side of the C ABI declared in include/moe_ffn.h: argument checks,
+// workspace layout, launch sizing (CU reserve) and the kernel launch.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/moe_ffn.h"
+#include "moe_ffn_kernel.h"
+#include "moe_ffn_layout.h"
+
+using moeffn::KParams;
+using moeffn::Layout;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Physical CU count per device: an immutable device property, queried once.
+std::atomic<int> g_cus[kMaxDevices];
+
+int physical_cus(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return -1;
+  int v = g_cus[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return -1;
+  g_cus[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+long env_long(const char* name, long dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  char* end = nullptr;
+  long v = std::strtol(s, &end, 10);
+  return (end && *end == '\0') ? v : dflt;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_problem(const moe_ffn_problem* p) {
+  if (!p) return MOE_FFN_ERR_INVALID_ARG;
+  if (p->max_tokens < 0 || p->hidden <= 0 || p->intermediate <= 0 || p->num_experts <= 0 || p->top_k <= 0)
+    return MOE_FFN_ERR_INVALID_ARG;
+  if (p->reserved_ != 0) return MOE_FFN_ERR_INVALID_ARG;
+  if (p->recipe < MOE_FFN_RECIPE_BF16 || p->recipe > MOE_FFN_RECIPE_FP8_FP4) return MOE_FFN_ERR_INVALID_ARG;
+  const int64_t kmul = p->recipe == MOE_FFN_RECIPE_BF16 ? 64 : 128;
+  if (p->hidden % kmul || p->intermediate % kmul) return MOE_FFN_ERR_UNSUPPORTED;
+  if (p->num_experts > moeffn::kMaxExperts || p->top_k > moeffn::kMaxTopK) return MOE_FFN_ERR_UNSUPPORTED;
+  if (p->hidden > (1 << 20) || p->intermediate > (1 << 20)) return MOE_FFN_ERR_UNSUPPORTED;
+  // slot indices are 32-bit
+  if (p->max_tokens * p->top_k + moeffn::kMaxBM >= (int64_t(1) << 31)) return MOE_FFN_ERR_UNSUPPORTED;
+  return MOE_FFN_OK;
+}
+
+// Token block of the GEMM tiles for this call: the average expert group
+// decides between weight streaming (16 tokens, every weight byte read once)
+// and larger blocks that reuse each weight tile across more tokens.
+int choose_block_m(int recipe, int64_t T, int64_t k, int64_t E) {
+  const double avg = E > 0 ? double(T) * double(k) / double(E) : 0.0;
+  int bm = avg <= 16.0 ? 16 : avg <= 40.0 ? 32 : avg <= 96.0 ? 64 : 128;
+  const int cap = moeffn::max_block_m(recipe);
+  return bm > cap ? cap : bm;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_launch_size(int physical, int reserved, int max_cus) {
+  if (physical <= 0) return 2;
+  const int res = reserved > 0 ? reserved : 0;
+  int limit = physical - res;
+  if (limit < 2) limit = 2;
+  int target = (max_cus > 0 && max_cus < limit) ? max_cus : limit;
+  target -= target % 2;
+  return target < 2 ? 2 : target;
+}
+
+int moe_ffn_get_workspace_size(const moe_ffn_problem* p, size_t* bytes) {
+  if (!bytes) return MOE_FFN_ERR_INVALID_ARG;
+  const int rc = check_problem(p);
+  if (rc) return rc;
+  *bytes = moeffn::make_layout(p->max_tokens, p->hidden, p->intermediate, p->num_experts, p->top_k, p->recipe).total;
+  return MOE_FFN_OK;
+}
+
+int moe_ffn_get_token_alignment(int32_t recipe, int64_t* alignment) {
+  if (!alignment || recipe < MOE_FFN_RECIPE_BF16 || recipe > MOE_FFN_RECIPE_FP8_FP4) return MOE_FFN_ERR_INVALID_ARG;
+  *alignment = 1;
+  return MOE_FFN_OK;
+}
+
+int moe_ffn_get_workspace_view(const moe_ffn_problem* p, moe_ffn_workspace_view* v) {
+  if (!v) return MOE_FFN_ERR_INVALID_ARG;
+  const int rc = check_problem(p);
+  if (rc) return rc;
+  const Layout L = moeffn::make_layout(p->max_tokens, p->hidden, p->intermediate, p->num_experts, p->top_k, p->recipe);
+  v->h = L.h;
+  v->h_sf = L.h_sf;
+  v->o = L.o;
+  v->h_row_bytes = L.h_row_bytes;
+  v->h_sf_row_bytes = L.h_sf_row_bytes;
+  v->o_row_bytes = L.o_row_bytes;
+  return MOE_FFN_OK;
+}
+
+const char* moe_ffn_strerror(int code) {
+  switch (code) {
+    case MOE_FFN_OK: return "ok";
+    case MOE_FFN_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_FFN_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_FFN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_FFN_ERR_HIP: return "HIP runtime error";
+    case MOE_FFN_STATUS_BAD_EXPERT_INDEX: return "status: expert index outside [-1, E) was masked";
+    case MOE_FFN_STATUS_TIMEOUT: return "status: grid barrier or readiness wait timed out";
+    case MOE_FFN_STATUS_DIRTY_WORKSPACE: return "status: workspace counters were not zero at entry";
+    default: return "unknown code";
+  }
+}
+
+int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (!a || !workspace) return MOE_FFN_ERR_INVALID_ARG;
+  const int recipe = p->recipe;
+  const bool bf16 = recipe == MOE_FFN_RECIPE_BF16;
+  const int64_t T = a->num_tokens;
+  if (T < 0 || T > p->max_tokens) return MOE_FFN_ERR_INVALID_ARG;
+  if (a->y_dtype != MOE_FFN_Y_BF16 && a->y_dtype != MOE_FFN_Y_FP32) return MOE_FFN_ERR_INVALID_ARG;
+  if (!a->w1 || !a->w2 || !aligned16(a->w1) || !aligned16(a->w2)) return MOE_FFN_ERR_INVALID_ARG;
+  if (!bf16 && (!a->w1_sf || !a->w2_sf || !aligned16(a->w1_sf) || !aligned16(a->w2_sf))) return MOE_FFN_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!a->x || !a->topk_idx || !a->topk_weights || !a->y) return MOE_FFN_ERR_INVALID_ARG;
+    if (!aligned16(a->x) || !aligned16(a->y) || !aligned16(a->topk_idx) || !aligned16(a->topk_weights))
+      return MOE_FFN_ERR_INVALID_ARG;
+    if (!bf16 && (!a->x_sf || !aligned16(a->x_sf))) return MOE_FFN_ERR_INVALID_ARG;
+  }
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MOE_FFN_ERR_INVALID_ARG;
+  const Layout L = moeffn::make_layout(p->max_tokens, p->hidden, p->intermediate, p->num_experts, p->top_k, recipe);
+  if (workspace_bytes < L.total) return MOE_FFN_ERR_WORKSPACE_TOO_SMALL;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_FFN_ERR_HIP;
+  const int cus = physical_cus(dev);
+  if (cus <= 0) return MOE_FFN_ERR_HIP;
+  const int reserve = a->reserved_cus >= 0 ? a->reserved_cus : (int)env_long("MOE_FFN_RESERVED_CUS", 2);
+  const int grid = moe_ffn_launch_size(cus, reserve, a->max_cus);
+  const long timeout_ms = env_long("MOE_FFN_BARRIER_TIMEOUT_MS", 2000);
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  KParams k{};
+  k.T = (int32_t)T;
+  k.H = (int32_t)p->hidden;
+  k.I = (int32_t)p->intermediate;
+  k.E = (int32_t)p->num_experts;
+  k.k = (int32_t)p->top_k;
+  k.y_fp32 = a->y_dtype == MOE_FFN_Y_FP32;
+  k.clamp_on = std::isfinite(a->activation_clamp) && a->activation_clamp > 0.0f;
+  k.clamp = k.clamp_on ? a->activation_clamp : 0.0f;
+  k.timeout_ticks = (uint64_t)(timeout_ms > 0 ? timeout_ms : 1) * 100000ull;
+  k.chunk_slots = L.chunk_slots;
+  k.x = static_cast<const uint8_t*>(a->x);
+  k.x_sf = a->x_sf;
+  k.idx = a->topk_idx;
+  k.tw = a->topk_weights;
+  k.w1 = static_cast<const uint8_t*>(a->w1);
+  k.w1_sf = a->w1_sf;
+  k.w2 = static_cast<const uint8_t*>(a->w2);
+  k.w2_sf = a->w2_sf;
+  k.y = a->y;
+  k.out_counts = a->expert_counts;
+  k.out_offsets = a->expert_offsets;
+  k.out_r2s = a->row_to_slot;
+  k.out_s2r = a->slot_to_row;
+  k.out_status = a->status;
+  k.ctrl = reinterpret_cast<moeffn::Ctrl*>(ws + L.ctrl);
+  k.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  k.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  k.hist = reinterpret_cast<int32_t*>(ws + L.hist);
+  k.r2s = reinterpret_cast<int32_t*>(ws + L.r2s);
+  k.s2r = reinterpret_cast<int32_t*>(ws + L.s2r);
+  k.ready = reinterpret_cast<uint32_t*>(ws + L.ready);
+  k.h = ws + L.h;
+  k.h_sf = ws + L.h_sf;
+  k.o = reinterpret_cast<float*>(ws + L.o);
+
+  const int bm = choose_block_m(recipe, T, p->top_k, p->num_experts);
+  if (env_long("MOE_FFN_LOG", 0) > 0)
+    std::fprintf(stderr, "moe_ffn: T=%lld recipe=%d grid=%d (CUs %d, reserve %d, cap %d) block_m=%d\n",
+                 (long long)T, recipe, grid, cus, reserve, a->max_cus, bm);
+  const hipError_t err = moeffn::launch_forward(recipe, bm, grid, k, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Device helpers for the fused MoE forward on gfx950 (CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moeffn {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------
+// Number formats
+// ---------------------------------------------------------------------------
+
+// fp32 -> OCP E4M3FN code, round to nearest even, saturating at +-448.
+// Normal range: round the fp32 mantissa to 3 bits on the integer pattern and
+// re-bias the exponent (127 -> 7).  Below 2^-6 the e4m3 grid is m * 2^-9, so
+// the code is rint(|q| * 512) (0..8; 8 is the smallest normal, code 0x08).
+__device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(q);
+  uint32_t code;
+  if (a < 0x1p-6f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    uint32_t b = __float_as_uint(a);
+    b += 0x7FFFFu + ((b >> 20) & 1u);
+    code = (b >> 20) - (120u << 3);
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return sign | code;
+}
+
+// fp32 -> bf16 bits, round to nearest even (overflow gives inf, NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Exponent E of the e8m0 scale of a 1x32 block: the smallest integer with
+// amax <= 448 * 2^E (448 = 1.75 * 2^8), clamped to [-127, 127]; 0 for an
+// all-zero block.  Exact on the fp32 bit pattern: with amax = f * 2^p,
+// f in [1, 2), E = p - 8 when f <= 1.75, else p - 7.
+__device__ __forceinline__ int block_scale_exp(float amax) {
+  if (!(amax > 0.0f)) return 0;
+  const uint32_t b = __float_as_uint(amax);
+  const int ef = (int)(b >> 23);
+  int E = (ef == 0) ? -127 : (ef - 127) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  E = E < -127 ? -127 : E;
+  E = E > 127 ? 127 : E;
+  return E;
+}
+
+// SwiGLU of one (gate, up) pair with the optional symmetric clamp of both.
+__device__ __forceinline__ float swiglu(float g, float u, bool clamp_on, float c) {
+  if (clamp_on) {
+    g = __builtin_fminf(__builtin_fmaxf(g, -c), c);
+    u = __builtin_fminf(__builtin_fmaxf(u, -c), c);
+  }
+  const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+  return g * sig * u;
+}
+
+// ---------------------------------------------------------------------------
+// Agent-scope synchronisation (the 8 XCDs have separate L2s: every hand-off
+// between workgroups goes through release/acquire at agent scope).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void fence_release() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+__device__ __forceinline__ uint32_t ld_acquire(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_release(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_acq_rel(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_release(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }  // 100 MHz
+
+// ---------------------------------------------------------------------------
+// Workgroup-wide exclusive scan of one int per thread (256 threads).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// `scratch` needs 4 ints of LDS.  Returns the exclusive prefix; *total gets the sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = wave_incl_scan(v);
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; w++) {
+    int s = scratch[w];
+    base += (w < wave) ? s : 0;
+    all += s;
+  }
+  __syncthreads();
+  *total = all;
+  return base + incl - v;
+}
+
+}  // namespace moeffn

@@ -1,0 +1,55 @@
+// Kernel parameter block and launcher of the fused MoE forward.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_ffn_layout.h"
+
+namespace moeffn {
+
+struct KParams {
+  // problem of this call
+  int32_t T, H, I, E, k;
+  int32_t y_fp32;
+  int32_t clamp_on;
+  float clamp;
+  uint64_t timeout_ticks;  // bound on every wait, in 100 MHz realtime ticks
+  int64_t chunk_slots;     // routing chunk size
+  // inputs
+  const uint8_t* x;
+  const uint8_t* x_sf;
+  const int32_t* idx;
+  const float* tw;
+  const uint8_t* w1;
+  const uint8_t* w1_sf;
+  const uint8_t* w2;
+  const uint8_t* w2_sf;
+  void* y;
+  // optional outputs
+  int32_t* out_counts;
+  int32_t* out_offsets;
+  int32_t* out_r2s;
+  int32_t* out_s2r;
+  int32_t* out_status;
+  // workspace views
+  Ctrl* ctrl;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* hist;
+  int32_t* r2s;
+  int32_t* s2r;
+  uint32_t* ready;
+  uint8_t* h;
+  uint8_t* h_sf;
+  float* o;
+};
+
+// Launches the persistent kernel for `recipe` with token block `bm` on `grid`
+// workgroups.  Returns the hipError_t of the launch.
+hipError_t launch_forward(int recipe, int bm, int grid, const KParams& p, hipStream_t stream);
+
+// Largest token block the recipe supports (register budget of the A ring).
+int max_block_m(int recipe);
+
+}  // namespace moeffn

@@ -1,0 +1,75 @@
+// Workspace layout of the fused MoE forward (host and device).
+//
+// The layout is a function of the problem only (max_tokens, H, I, E, k,
+// recipe): never of the CU count or the reserve, so a caller may cache one
+// workspace per problem shape and change the reserve freely.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeffn {
+
+constexpr int kThreads = 256;          // one workgroup = 4 waves of 64
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 64;
+constexpr int kMaxChunks = 256;        // routing chunks (one per thread in the column scan)
+constexpr int kMinChunkSlots = 1024;   // routing chunk granularity
+constexpr int kMinBM = 16;             // smallest token block of any tile config
+constexpr int kMaxBM = 128;            // largest token block (h rows are padded by this)
+constexpr int kNumBarriers = 4;
+
+// Control block at workspace offset 0.  Every field is zero between calls.
+struct Ctrl {
+  uint32_t bar[kNumBarriers];  // grid barrier arrival counters
+  uint32_t exit_count;         // workgroups that reached the end of the call
+  uint32_t tile_next;          // next GEMM tile to claim
+  uint32_t abort;              // set on a fatal condition: every wait gives up
+  int32_t status;              // first MOE_FFN_STATUS_* of the call
+  uint32_t pad[56];
+};
+static_assert(sizeof(Ctrl) == 256, "control block must stay 256 bytes");
+static_assert(offsetof(Ctrl, bar) == 0, "barrier counters lead the control block");
+static_assert(offsetof(Ctrl, exit_count) == 16, "layout change must be deliberate");
+static_assert(offsetof(Ctrl, status) == 28, "layout change must be deliberate");
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+  size_t ctrl, counts, offsets, hist, r2s, s2r, ready, h, h_sf, o, total;
+  int64_t chunk_slots;   // slots per routing chunk
+  int64_t max_slots;     // max_tokens * k
+  int64_t ready_len;     // readiness counters (one per token block of any expert)
+  int64_t h_rows;        // rows of h (max_slots + kMaxBM padding)
+  int64_t h_row_bytes, h_sf_row_bytes, o_row_bytes;
+};
+
+// recipe: 0 bf16, 1 fp8xfp8, 2 fp8xfp4 (h is bf16 for recipe 0, e4m3 otherwise)
+inline Layout make_layout(int64_t max_tokens, int64_t H, int64_t I, int64_t E, int64_t k, int recipe) {
+  Layout L{};
+  const size_t A = 256;
+  L.max_slots = max_tokens * k;
+  int64_t per = (L.max_slots + kMaxChunks - 1) / kMaxChunks;
+  L.chunk_slots = per <= kMinChunkSlots ? kMinChunkSlots
+                                        : (per + kMinChunkSlots - 1) / kMinChunkSlots * kMinChunkSlots;
+  L.ready_len = (L.max_slots + kMinBM - 1) / kMinBM + E;
+  L.h_rows = L.max_slots + kMaxBM;
+  L.h_row_bytes = recipe == 0 ? I * 2 : I;
+  L.h_sf_row_bytes = recipe == 0 ? 0 : I / 32;
+  L.o_row_bytes = H * 4;
+  size_t off = 0;
+  L.ctrl = off;    off = align_up(off + sizeof(Ctrl), A);
+  L.counts = off;  off = align_up(off + sizeof(int32_t) * (size_t)E, A);
+  L.offsets = off; off = align_up(off + sizeof(int32_t) * (size_t)(E + 1), A);
+  L.hist = off;    off = align_up(off + sizeof(int32_t) * (size_t)kMaxChunks * (size_t)E, A);
+  L.r2s = off;     off = align_up(off + sizeof(int32_t) * (size_t)(L.max_slots + 1), A);
+  L.s2r = off;     off = align_up(off + sizeof(int32_t) * (size_t)(L.max_slots + 1), A);
+  L.ready = off;   off = align_up(off + sizeof(uint32_t) * (size_t)L.ready_len, A);
+  L.h = off;       off = align_up(off + (size_t)L.h_rows * (size_t)L.h_row_bytes, A);
+  L.h_sf = off;    off = align_up(off + (size_t)L.h_rows * (size_t)L.h_sf_row_bytes, A);
+  L.o = off;       off = align_up(off + (size_t)(L.max_slots > 0 ? L.max_slots : 1) * (size_t)L.o_row_bytes, A);
+  L.total = off;
+  return L;
+}
+
+}  // namespace moeffn

@@ -68,7 +68,8 @@ def lib():
             ("oracle_route", ctypes.c_int, [P, i64, i64, i64, P, P, P, P]),
             ("oracle_forward", ctypes.c_int, [P] + [P] * 14),
             ("oracle_forward_tokens", ctypes.c_int, [P] + [P] * 8 + [P, i64, P]),
-            ("oracle_ffn_row", ctypes.c_int, [P, P, P, i64, i64, P, P, P, P, P, P, P, P, P, P]),
+            ("oracle_forward_tokens_band", ctypes.c_int, [P] + [P] * 8 + [P, i64, P, d, P]),
+            ("oracle_ffn_row", ctypes.c_int, [P, P, P, i64, i64, P, P, P, P, P, P, P, P, P, P, d, P]),
             ("oracle_num_threads", ctypes.c_int, []),
         ]:
             fn = getattr(L, name)
@@ -167,8 +168,31 @@ def forward_tokens(p: dict, tokens, y_fp32: bool, clamp: float):
     return y, rc
 
 
-def ffn_row(p: dict, t: int, e: int, clamp: float):
-    """Intermediates of one routed row: L1 output, activation, re-quantised h, h codes/scales, L2 output."""
+def forward_tokens_band(p: dict, tokens, y_fp32: bool, clamp: float, rho: float):
+    """Per-token forward plus the allowance of re-quantisation decisions within band rho.
+
+    Returns (y_rows, allow_rows, status): allow_rows[q, n] bounds how far y can
+    move when an implementation whose L1 result differs from the exact one by
+    a relative rho picks the other grid point (or block exponent) for elements
+    that lie that close to a rounding boundary.
+    """
+    T, H, I, E, k, recipe = p["T"], p["H"], p["I"], p["E"], p["k"], p["recipe"]
+    x, x_sf, idx, w, w1, w1_sf, w2, w2_sf = _args(p)
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    y = np.zeros((len(toks), H), np.float32 if y_fp32 else np.uint16)
+    allow = np.zeros((len(toks), H), np.float64)
+    prob = _problem(T, H, I, E, k, recipe, y_fp32, clamp)
+    rc = lib().oracle_forward_tokens_band(ctypes.byref(prob), _ptr(x), _ptr(x_sf), _ptr(idx), _ptr(w),
+                                          _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
+                                          _ptr(toks), len(toks), _ptr(y), float(rho), _ptr(allow))
+    if rc < 0:
+        raise RuntimeError(f"oracle_forward_tokens_band failed: {rc}")
+    return y, allow, rc
+
+
+def ffn_row(p: dict, t: int, e: int, clamp: float, rho: float = 0.0):
+    """Intermediates of one routed row: L1 output, activation, re-quantised h, h codes/scales, L2 output,
+    and the rounding-decision band of each re-quantised element for `rho`."""
     T, H, I, E, k, recipe = p["T"], p["H"], p["I"], p["E"], p["k"], p["recipe"]
     x, x_sf, idx, w, w1, w1_sf, w2, w2_sf = _args(p)
     c = np.zeros(2 * I, np.float32)
@@ -177,13 +201,15 @@ def ffn_row(p: dict, t: int, e: int, clamp: float):
     codes = np.zeros(I, np.uint16 if recipe == RECIPE_BF16 else np.uint8)
     hsf = np.zeros(I // 32, np.uint8)
     o = np.zeros(H, np.float32)
+    delta = np.zeros(I, np.float64)
     prob = _problem(T, H, I, E, k, recipe, 1, clamp)
     rc = lib().oracle_ffn_row(ctypes.byref(prob), _ptr(x), _ptr(x_sf), int(t), int(e),
                               _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
-                              _ptr(c), _ptr(h), _ptr(hq), _ptr(codes), _ptr(hsf), _ptr(o))
+                              _ptr(c), _ptr(h), _ptr(hq), _ptr(codes), _ptr(hsf), _ptr(o),
+                              float(rho), _ptr(delta))
     if rc < 0:
         raise RuntimeError(f"oracle_ffn_row failed: {rc}")
-    return {"c": c, "h": h, "hq": hq, "h_codes": codes, "h_sf": hsf, "o": o}
+    return {"c": c, "h": h, "hq": hq, "h_codes": codes, "h_sf": hsf, "o": o, "delta": delta}
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

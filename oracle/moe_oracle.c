@@ -231,9 +231,62 @@ static double dot(const double* a, const double* b, int64_t n) {
 /*   hq_sf [I/32] e8m0 bytes (optional; FP8 recipes only)                    */
 /*   o_out  [H]  fp32 L2 output (required)                                   */
 /* ------------------------------------------------------------------------ */
+/* Spacing of the E4M3 grid around |v| (v finite, |v| <= 448). */
+static double e4m3_spacing(double v) {
+    int e;
+    double a = fabs(v);
+    if (a < ldexp(1.0, -6)) return ldexp(1.0, -9);
+    frexp(a, &e);
+    e -= 1;
+    if (e > 8) e = 8;
+    return ldexp(1.0, e - 3);
+}
+
+/* Rounding-decision band (parity infrastructure, not part of the method).
+   The re-quantisation turns the fp32 activation into a code.  An
+   implementation whose L1 outputs differ from the exact ones by at most
+   rho * RMS(L1 row) per element sees each activation move by at most
+   band_i = rho * RMS * (1.1 |u_i| + |silu(g_i)|)   (|silu'| <= 1.1),
+   so it may pick the other grid neighbour of an element whose exact value
+   lies within band_i of a rounding midpoint, and the other block exponent
+   when the block amax lies within the largest band of the block of a
+   boundary 448 * 2^E.  delta[i] receives the largest resulting change of the
+   dequantised value: one grid spacing, two spacings at the coarser exponent
+   for an ambiguous block exponent, 0 for an unambiguous element. */
+static void requant_band(const float* h, const float* c, int64_t I, double rho, float clamp, double* delta) {
+    int64_t b, i;
+    double rms = 0.0, cc = clamp;
+    int clamp_on = isfinite(cc) && cc > 0.0;
+    for (i = 0; i < 2 * I; i++) rms += (double)c[i] * (double)c[i];
+    rms = sqrt(rms / (double)(2 * I));
+    for (b = 0; b < I / 32; b++) {
+        double amax = 0.0, bmax = 0.0, band[32];
+        int E, scale_amb;
+        for (i = 32 * b; i < 32 * b + 32; i++) {
+            double g = c[i], u = c[I + i];
+            if (clamp_on) { g = fmin(fmax(g, -cc), cc); u = fmin(fmax(u, -cc), cc); }
+            band[i - 32 * b] = rho * rms * (1.1 * fabs(u) + fabs(g / (1.0 + exp(-g))));
+            if (band[i - 32 * b] > bmax) bmax = band[i - 32 * b];
+            if (fabs((double)h[i]) > amax) amax = fabs((double)h[i]);
+        }
+        E = oracle_scale_exp(amax);
+        scale_amb = amax > 0.0 && (fabs(amax - ldexp(448.0, E)) <= bmax || fabs(amax - ldexp(448.0, E - 1)) <= bmax);
+        for (i = 32 * b; i < 32 * b + 32; i++) {
+            double q = ldexp((double)h[i], -E);
+            double sp = e4m3_spacing(q);
+            double lo = floor(q / sp) * sp;       /* grid neighbours of q (exact: sp is a power of two) */
+            double mid = lo + 0.5 * sp;
+            if (scale_amb) delta[i] = 2.0 * ldexp(e4m3_spacing(ldexp((double)h[i], -(E + 1))), E + 1);
+            else if (ldexp(fabs(q - mid), E) <= band[i - 32 * b]) delta[i] = ldexp(sp, E);
+            else delta[i] = 0.0;
+        }
+    }
+}
+
 static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, int64_t t, int64_t e,
                    const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
-                   float* c_out, float* h_out, double* hq_out, void* hq_codes, uint8_t* hq_sf, float* o_out) {
+                   float* c_out, float* h_out, double* hq_out, void* hq_codes, uint8_t* hq_sf, float* o_out,
+                   double rho, double* o_allow, double* delta_out) {
     const int64_t H = p->hidden, I = p->intermediate;
     double* xd = (double*)malloc(sizeof(double) * (size_t)H);
     double* wd = (double*)malloc(sizeof(double) * (size_t)(H > I ? H : I));
@@ -277,9 +330,28 @@ static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
     }
     /* O6: L2 = hq . W2[e]^T over the intermediate dimension, exact in double,
        rounded once to fp32 (the per-slot result stays fp32 until the combine). */
-    for (n = 0; n < H; n++) {
-        dequant_weight_row(p->recipe, w2, w2_sf, e * H + n, I, wd);
-        o_out[n] = (float)dot(hq, wd, I);
+    {
+        double* delta = NULL;
+        if ((o_allow || delta_out) && p->recipe != OR_RECIPE_BF16) {
+            delta = (double*)calloc((size_t)I, sizeof(double));
+            if (!delta) { free(xd); free(wd); free(c); free(h); free(hq); return OR_NO_MEMORY; }
+            requant_band(h, c, I, rho, p->activation_clamp, delta);
+        }
+        for (n = 0; n < H; n++) {
+            dequant_weight_row(p->recipe, w2, w2_sf, e * H + n, I, wd);
+            o_out[n] = (float)dot(hq, wd, I);
+            if (o_allow) {
+                double a = 0.0;
+                if (delta)
+                    for (i = 0; i < I; i++)
+                        if (delta[i] != 0.0) a += delta[i] * fabs(wd[i]);
+                o_allow[n] = a;
+            }
+        }
+        if (delta_out) {
+            for (i = 0; i < I; i++) delta_out[i] = delta ? delta[i] : 0.0;
+        }
+        free(delta);
     }
     if (c_out) memcpy(c_out, c, sizeof(float) * (size_t)(2 * I));
     if (h_out) memcpy(h_out, h, sizeof(float) * (size_t)I);
@@ -377,7 +449,8 @@ int oracle_forward(const oracle_problem* p, const void* x, const uint8_t* x_sf,
     for (r = 0; r < R; r++) {
         int64_t e = 0;
         while (offsets[e + 1] <= r) e++;
-        if (ffn_row(p, x, x_sf, r2s[r] / k, e, w1, w1_sf, w2, w2_sf, NULL, NULL, NULL, NULL, NULL, o + r * H) != OR_OK)
+        if (ffn_row(p, x, x_sf, r2s[r] / k, e, w1, w1_sf, w2, w2_sf, NULL, NULL, NULL, NULL, NULL, o + r * H,
+                    0.0, NULL, NULL) != OR_OK)
             err |= 1;
     }
     if (err) { free(counts); free(offsets); free(r2s); free(s2r); free(o); return OR_NO_MEMORY; }
@@ -407,12 +480,15 @@ int oracle_forward(const oracle_problem* p, const void* x, const uint8_t* x_sf,
  * of expert topk_idx[t, j] directly for every valid j and combine.  Rows of
  * y_rows follow the order of `tokens`.  Used for sampled checks at sizes the
  * routed forward cannot reach in seconds, and as an independent path to the
- * routed one.
+ * routed one.  When allow_rows is not NULL it receives, per output element,
+ * sum_j |w_j| * sum_i delta_i |W2(e_j, n, i)|: the largest change of y that
+ * re-quantisation decisions inside the band `rho` can cause (requant_band).
  */
-int oracle_forward_tokens(const oracle_problem* p, const void* x, const uint8_t* x_sf,
-                          const int32_t* topk_idx, const float* topk_w,
-                          const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
-                          const int64_t* tokens, int64_t ntok, void* y_rows) {
+int oracle_forward_tokens_band(const oracle_problem* p, const void* x, const uint8_t* x_sf,
+                               const int32_t* topk_idx, const float* topk_w,
+                               const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
+                               const int64_t* tokens, int64_t ntok, void* y_rows,
+                               double rho, double* allow_rows) {
     int64_t H, E, k, q;
     int err = 0, bad = 0;
     if (check_problem(p) != OR_OK) return OR_BAD_ARG;
@@ -423,36 +499,55 @@ int oracle_forward_tokens(const oracle_problem* p, const void* x, const uint8_t*
     for (q = 0; q < ntok; q++) {
         int64_t t = tokens[q], j, n;
         float* o = (float*)malloc(sizeof(float) * (size_t)(k * H));
-        if (!o) { err |= 1; continue; }
+        double* oa = allow_rows ? (double*)calloc((size_t)(k * H), sizeof(double)) : NULL;
+        if (!o || (allow_rows && !oa)) { free(o); free(oa); err |= 1; continue; }
         for (j = 0; j < k; j++) {
             int32_t e = topk_idx[t * k + j];
             if (e >= 0 && e < E) {
-                if (ffn_row(p, x, x_sf, t, e, w1, w1_sf, w2, w2_sf, NULL, NULL, NULL, NULL, NULL, o + j * H) != OR_OK) err |= 1;
+                if (ffn_row(p, x, x_sf, t, e, w1, w1_sf, w2, w2_sf, NULL, NULL, NULL, NULL, NULL, o + j * H,
+                            rho, oa ? oa + j * H : NULL, NULL) != OR_OK) err |= 1;
             } else if (e != -1) {
                 bad |= 1;
             }
         }
         for (n = 0; n < H; n++) {
-            double acc = 0.0;
+            double acc = 0.0, al = 0.0;
             for (j = 0; j < k; j++) {
                 int32_t e = topk_idx[t * k + j];
-                if (e >= 0 && e < E) acc += (double)topk_w[t * k + j] * (double)o[j * H + n];
+                if (e >= 0 && e < E) {
+                    acc += (double)topk_w[t * k + j] * (double)o[j * H + n];
+                    if (oa) al += fabs((double)topk_w[t * k + j]) * oa[j * H + n];
+                }
             }
             store_y(p, y_rows, q, n, acc);
+            if (allow_rows) allow_rows[q * H + n] = al;
         }
         free(o);
+        free(oa);
     }
     if (err) return OR_NO_MEMORY;
     return bad ? OR_BAD_EXPERT_INDEX : OR_OK;
 }
 
-/* One row's intermediates (token t through expert e), for unit checks. */
+int oracle_forward_tokens(const oracle_problem* p, const void* x, const uint8_t* x_sf,
+                          const int32_t* topk_idx, const float* topk_w,
+                          const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
+                          const int64_t* tokens, int64_t ntok, void* y_rows) {
+    return oracle_forward_tokens_band(p, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, tokens, ntok, y_rows,
+                                      0.0, NULL);
+}
+
+/* One row's intermediates (token t through expert e), for unit checks;
+   delta_out (optional, [I]) receives the rounding-decision band of each
+   re-quantised element for the given rho (see requant_band). */
 int oracle_ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, int64_t t, int64_t e,
                    const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
-                   float* c_out, float* h_out, double* hq_out, void* hq_codes, uint8_t* hq_sf, float* o_out) {
+                   float* c_out, float* h_out, double* hq_out, void* hq_codes, uint8_t* hq_sf, float* o_out,
+                   double rho, double* delta_out) {
     if (check_problem(p) != OR_OK) return OR_BAD_ARG;
     if (t < 0 || t >= p->num_tokens || e < 0 || e >= p->num_experts || !o_out) return OR_BAD_ARG;
-    return ffn_row(p, x, x_sf, t, e, w1, w1_sf, w2, w2_sf, c_out, h_out, hq_out, hq_codes, hq_sf, o_out);
+    return ffn_row(p, x, x_sf, t, e, w1, w1_sf, w2, w2_sf, c_out, h_out, hq_out, hq_codes, hq_sf, o_out,
+                   rho, NULL, delta_out);
 }
 
 int oracle_num_threads(void) {

@@ -1,0 +1,219 @@
+"""GPU parity of the HIP forward against the CPU oracle (MI355X only).
+
+Routing outputs must match bit for bit; y must stay within the bounds
+max|y - y_ref| <= 2e-2 RMS(y_ref) (FP8 recipes) and 5e-3 RMS(y_ref) (BF16,
+fp32 y), y_ref being the oracle's rounded output.  Every call goes through
+the C ABI (moe_ffn_forward) via the Python binding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_ffn_histogram_amd import synth
+from gpu_common import (Runner, assert_h_decisions, assert_y_parity, log, oracle_y, oracle_y_band,
+                        rel_err, tol_for, upload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_tables(run: Runner, p: dict, T: int):
+    idx = p["topk_idx"][:T]
+    counts, offsets, r2s, s2r, _ = oracle.route(idx, p["E"])
+    g_counts, g_off, g_r2s, g_s2r = run.tables(T)
+    assert np.array_equal(g_counts, counts)
+    assert np.array_equal(g_off, offsets)
+    assert np.array_equal(g_r2s, r2s)
+    assert np.array_equal(g_s2r, s2r)
+
+
+def _small_cfg(recipe, T, H, I, E, k, routing="softmax", seed=7, y_fp32=False):
+    return synth.Config(f"r{recipe}_T{T}_H{H}_I{I}_E{E}_k{k}", recipe, T, H, I, E, k, routing, seed, y_fp32=y_fp32)
+
+
+@pytest.mark.parametrize("T", [0, 8, 48, 192, 1000])
+def test_routing_bitexact_with_masks(T):
+    cfg = _small_cfg(synth.RECIPE_FP8_FP4, max(T, 1), 256, 128, 16, 4, "uniform", seed=31)
+    p = synth.make_problem(cfg, T=max(T, 1), threads=4)
+    if T:
+        rng = np.random.default_rng(T)
+        p["topk_idx"][rng.random(p["topk_idx"].shape) < 0.1] = -1
+    p["T"] = max(T, 1)
+    log(f"routing T={T}")
+    run = Runner(p)
+    run.run(num_tokens=T)
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    _check_tables(run, p, T)
+    if T == 0:
+        assert int(run.counts.sum().item()) == 0
+        assert bool((run.y == -12345).all())
+
+
+@pytest.mark.parametrize("y_fp32", [True, False])
+def test_bf16_recipe_full(y_fp32):
+    cfg = synth.CONFIGS["bf16_T64_H256_I128_E8_k2"]
+    p = synth.make_problem(cfg, threads=4)
+    log(f"bf16 T64 y_fp32={y_fp32}")
+    run = Runner(p, y_fp32=y_fp32)
+    run.run()
+    torch.cuda.synchronize()
+    _check_tables(run, p, p["T"])
+    ref = oracle_y(p, y_fp32, p["clamp"])
+    got = run.y_float()
+    err, rms = rel_err(got, ref)
+    log(f"  max|dy|/rms = {err:.3e}")
+    if y_fp32:
+        assert err <= 5e-3
+    else:
+        # one bf16 rounding step of y may flip on either side
+        assert np.all(np.abs(got - ref) <= 5e-3 * rms + np.abs(ref) * 2.0 ** -8)
+
+
+def test_fp8xfp8_config_full():
+    cfg = synth.CONFIGS["fp8xfp8_T512_H2048_I768_E64_k6"]
+    p = synth.make_problem(cfg, threads=8)
+    log("fp8xfp8 T512 full")
+    run = Runner(p)
+    run.run()
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    _check_tables(run, p, p["T"])
+    ref, allow = oracle_y_band(p, False, p["clamp"])
+    assert_y_parity(run.y_float(), ref, allow, 2e-2, "fp8xfp8 T512")
+    flips = assert_h_decisions(run, p, range(0, p["T"] * p["k"], 97), p["clamp"])
+    log(f"  near-tie code flips in sampled rows: {flips}")
+
+
+@pytest.mark.parametrize("T,E,k", [(96, 32, 8), (40, 8, 4), (333, 8, 3), (1000, 4, 2), (2048, 8, 4)])
+def test_fp8xfp4_reduced_full(T, E, k):
+    # spans token-block sizes 16..128 (average rows per expert 24 .. 1024) and ragged tails
+    cfg = _small_cfg(synth.RECIPE_FP8_FP4, T, 1024, 512, E, k, "softmax", seed=T + E)
+    p = synth.make_problem(cfg, threads=8)
+    log(f"fp8xfp4 reduced T={T} E={E} k={k}")
+    run = Runner(p)
+    run.run()
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    _check_tables(run, p, T)
+    ref, allow = oracle_y_band(p, False, p["clamp"])
+    assert_y_parity(run.y_float(), ref, allow, 2e-2, f"fp8xfp4 T={T}")
+    R = int(run.offsets[-1].item())
+    flips = assert_h_decisions(run, p, list(range(0, R, max(1, R // 40))) + [R - 1], p["clamp"])
+    log(f"  near-tie code flips in sampled rows: {flips}")
+
+
+def test_deepseek_T128_sampled():
+    cfg = synth.CONFIGS["deepseek_fp8xfp4_T128"]
+    p = synth.make_problem(cfg, threads=16)
+    log("deepseek T128 (full shape), sampled tokens")
+    run = Runner(p)
+    run.run()
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    _check_tables(run, p, p["T"])
+    toks = [0, 1, 2, 63, 64, 100, 126, 127] + list(np.random.default_rng(0).choice(128, 8, replace=False))
+    ref, allow = oracle_y_band(p, False, p["clamp"], tokens=toks)
+    assert_y_parity(run.y_float()[toks], ref, allow, 2e-2, "deepseek T128")
+    flips = assert_h_decisions(run, p, [0, 100, 511, 777, 1023], p["clamp"])
+    log(f"  near-tie code flips in sampled rows: {flips}")
+
+
+def test_deterministic_and_grid_size_invariant():
+    cfg = _small_cfg(synth.RECIPE_FP8_FP4, 700, 1024, 512, 16, 6, "uniform", seed=5)
+    p = synth.make_problem(cfg, threads=8)
+    run = Runner(p)
+    outs = []
+    for reserve, cap in [(2, 0), (2, 0), (0, 0), (64, 0), (2, 40), (200, 0)]:
+        log(f"determinism reserve={reserve} cap={cap}")
+        run.run(reserved_cus=reserve, max_cus=cap)
+        torch.cuda.synchronize()
+        assert int(run.status.item()) == 0
+        outs.append(run.y.clone())
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_bad_expert_index_reported_and_masked():
+    cfg = _small_cfg(synth.RECIPE_FP8_FP8, 64, 256, 128, 8, 2, "uniform", seed=3)
+    p = synth.make_problem(cfg, threads=4)
+    p["topk_idx"][5, 1] = 9
+    p["topk_idx"][7, 0] = -4
+    run = Runner(p)
+    run.run()
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 1
+    q = dict(p, topk_idx=p["topk_idx"].copy())
+    q["topk_idx"][(q["topk_idx"] < -1) | (q["topk_idx"] >= 8)] = -1
+    _check_tables(run, q, 64)
+    ref, allow = oracle_y_band(q, False, p["clamp"])
+    assert_y_parity(run.y_float(), ref, allow, 2e-2, "bad index")
+    # the next call on the same workspace is clean
+    p2 = dict(q)
+    run.p = p2
+    upload_inputs(p2, run.d)
+    run.run()
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+
+
+def test_num_tokens_below_capacity_leaves_tail_rows():
+    cfg = _small_cfg(synth.RECIPE_FP8_FP4, 200, 512, 256, 8, 2, "softmax", seed=11)
+    p = synth.make_problem(cfg, threads=4)
+    run = Runner(p)
+    run.run(num_tokens=77)
+    torch.cuda.synchronize()
+    assert bool((run.y[77:] == -12345).all())
+    q = dict(p, T=77, x=p["x"][:77], x_sf=p["x_sf"][:77], topk_idx=p["topk_idx"][:77],
+             topk_weights=p["topk_weights"][:77])
+    _check_tables(run, q, 77)
+    ref, allow = oracle_y_band(q, False, p["clamp"])
+    assert_y_parity(run.y_float(77), ref, allow, 2e-2, "T=77 of 200")
+
+
+def test_clamp_engaged_and_off():
+    cfg = _small_cfg(synth.RECIPE_FP8_FP4, 64, 512, 256, 8, 2, "softmax", seed=13)
+    p = synth.make_problem(cfg, threads=4)
+    p["x_sf"] = (p["x_sf"].astype(np.int32) + 4).astype(np.uint8)  # x scaled by 16: |L1| >> 7
+    run = Runner(p)
+    for c in (7.0, 0.0):
+        log(f"clamp {c}")
+        run.run(clamp=c)
+        torch.cuda.synchronize()
+        ref, allow = oracle_y_band(p, False, c)
+        assert_y_parity(run.y_float(), ref, allow, 2e-2, f"clamp {c}")
+        assert_h_decisions(run, p, range(0, 128, 9), c)
+
+
+def test_graph_replay_changed_inputs_matches_eager():
+    cfg = _small_cfg(synth.RECIPE_FP8_FP4, 256, 1024, 512, 16, 4, "softmax", seed=21)
+    p = synth.make_problem(cfg, threads=8)
+    run = Runner(p)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run.run(stream=s, sentinel=False)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run.run(stream=torch.cuda.current_stream(), sentinel=False)
+    for r in range(6):
+        q = synth.with_inputs(p, cfg, seed=1000 + r)
+        if r == 3:
+            q["topk_idx"][::3, 1] = -1
+        upload_inputs(q, run.d)
+        run.y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        y_graph = run.y.clone()
+        st = int(run.status.item())
+        run.p = q
+        run.run(sentinel=False)
+        torch.cuda.synchronize()
+        log(f"replay {r}: status {st}")
+        assert st == 0
+        assert torch.equal(y_graph, run.y), f"replay {r} differs from eager"
+        _check_tables(run, q, q["T"])
+        ref, allow = oracle_y_band(q, False, q["clamp"])
+        assert_y_parity(run.y_float(), ref, allow, 2e-2, f"replay {r}")

@@ -424,3 +424,35 @@ def test_token_without_valid_slot_is_zero_and_t0_is_noop():
              topk_idx=p["topk_idx"][:0].copy(), topk_weights=p["topk_weights"][:0].copy())
     out = oracle.forward(q, True, 7.0, want_tables=True)
     assert out["y"].shape == (0, p["H"]) and out["counts"].sum() == 0
+
+
+# --------------------------------------------------------------------------
+# rounding-decision band (parity infrastructure): hand-derived closed form
+# --------------------------------------------------------------------------
+def test_band_allowance_closed_form():
+    gold = json.load(open(os.path.join(GOLDEN, "closed_form_example.json")))["band"]["expected"]
+    p = _closed_form_problem()
+    for rho, exp in gold.items():
+        y, allow, rc = oracle.forward_tokens_band(p, [0, 1], True, 7.0, float(rho))
+        assert rc == oracle.OK
+        assert np.all(allow[0] == exp[0]) and np.all(allow[1] == exp[1]), rho
+        assert np.array_equal(y, oracle.forward(p, True, 7.0)["y"])
+
+
+def test_band_is_monotone_zero_at_zero_and_absent_for_bf16():
+    p = _small(synth.RECIPE_FP8_FP4, T=8)
+    toks = list(range(8))
+    prev = None
+    for rho in (0.0, 2.0 ** -14, 2.0 ** -12, 2.0 ** -8):
+        _, allow, _ = oracle.forward_tokens_band(p, toks, False, 7.0, rho)
+        if rho == 0.0:
+            assert np.all(allow == 0.0)
+        if prev is not None:
+            assert np.all(allow >= prev)
+        prev = allow
+    assert prev.max() > 0.0
+    q = _small(synth.RECIPE_BF16, T=4)
+    _, allow, _ = oracle.forward_tokens_band(q, [0, 1, 2, 3], True, 7.0, 0.1)
+    assert np.all(allow == 0.0)
+    row = oracle.ffn_row(p, 0, int(p["topk_idx"][0, 0]), 7.0, rho=2.0 ** -8)
+    assert np.all((row["delta"] == 0.0) | (row["delta"] > 0.0))
