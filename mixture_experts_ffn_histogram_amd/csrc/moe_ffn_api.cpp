@@ -183,12 +183,14 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   k.hist = reinterpret_cast<int32_t*>(ws + L.hist);
   k.r2s = reinterpret_cast<int32_t*>(ws + L.r2s);
   k.s2r = reinterpret_cast<int32_t*>(ws + L.s2r);
-  k.ready = reinterpret_cast<uint32_t*>(ws + L.ready);
   k.h = ws + L.h;
   k.h_sf = ws + L.h_sf;
   k.o = reinterpret_cast<float*>(ws + L.o);
 
-  const int bm = choose_block_m(recipe, T, p->top_k, p->num_experts);
+  int bm = choose_block_m(recipe, T, p->top_k, p->num_experts);
+  const long bm_env = env_long("MOE_FFN_BLOCK_M", 0);  // tuning override: 16, 32, 64 or 128
+  if ((bm_env == 16 || bm_env == 32 || bm_env == 64 || bm_env == 128) && bm_env <= moeffn::max_block_m(recipe))
+    bm = (int)bm_env;
   if (env_long("MOE_FFN_LOG", 0) > 0)
     std::fprintf(stderr, "moe_ffn: T=%lld recipe=%d grid=%d (CUs %d, reserve %d, cap %d) block_m=%d\n",
                  (long long)T, recipe, grid, cus, reserve, a->max_cus, bm);

@@ -11,6 +11,28 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
+// Explicit global-address-space accesses.  A pointer that reaches a load
+// through LDS or a select is generic (flat) to the compiler, and a pending
+// flat load forces a full vmcnt drain before the next use of any load; these
+// helpers keep every device-memory access a global_* instruction.
+typedef __attribute__((address_space(1))) const v4i gv4i_c;
+typedef __attribute__((address_space(1))) v4i gv4i;
+typedef __attribute__((address_space(1))) const uint32_t gu32_c;
+typedef __attribute__((address_space(1))) uint32_t gu32;
+typedef __attribute__((address_space(1))) uint8_t gu8;
+typedef __attribute__((address_space(1))) v4f gv4f;
+typedef __attribute__((address_space(1))) const v4f gv4f_c;
+typedef __attribute__((address_space(1))) uint64_t gu64;
+
+__device__ __forceinline__ v4i ldg16(const void* p) { return *(gv4i_c*)p; }
+__device__ __forceinline__ v4i ldg16_nt(const void* p) { return __builtin_nontemporal_load((gv4i_c*)p); }
+__device__ __forceinline__ uint32_t ldg4(const void* p) { return *(gu32_c*)p; }
+__device__ __forceinline__ v4f ldg16f(const void* p) { return *(gv4f_c*)p; }
+__device__ __forceinline__ void stg16f(void* p, v4f v) { *(gv4f*)p = v; }
+__device__ __forceinline__ void stg4(void* p, uint32_t v) { *(gu32*)p = v; }
+__device__ __forceinline__ void stg1(void* p, uint8_t v) { *(gu8*)p = v; }
+__device__ __forceinline__ void stg8(void* p, uint32_t lo, uint32_t hi) { *(gu64*)p = ((uint64_t)hi << 32) | lo; }
+
 // ---------------------------------------------------------------------------
 // Number formats
 // ---------------------------------------------------------------------------

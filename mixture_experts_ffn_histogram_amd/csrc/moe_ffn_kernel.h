@@ -39,7 +39,6 @@ struct KParams {
   int32_t* hist;
   int32_t* r2s;
   int32_t* s2r;
-  uint32_t* ready;
   uint8_t* h;
   uint8_t* h_sf;
   float* o;

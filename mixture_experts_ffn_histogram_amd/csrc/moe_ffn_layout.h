@@ -17,29 +17,30 @@ constexpr int kMaxChunks = 256;        // routing chunks (one per thread in the 
 constexpr int kMinChunkSlots = 1024;   // routing chunk granularity
 constexpr int kMinBM = 16;             // smallest token block of any tile config
 constexpr int kMaxBM = 128;            // largest token block (h rows are padded by this)
-constexpr int kNumBarriers = 4;
+constexpr int kNumBarriers = 6;
+constexpr int kLocalRouteSlots = 4096;  // up to this many slots every workgroup routes on its own (in LDS)
 
 // Control block at workspace offset 0.  Every field is zero between calls.
 struct Ctrl {
   uint32_t bar[kNumBarriers];  // grid barrier arrival counters
   uint32_t exit_count;         // workgroups that reached the end of the call
-  uint32_t tile_next;          // next GEMM tile to claim
+  uint32_t tile_next;          // next L1 tile to claim
+  uint32_t tile_next2;         // next L2 tile to claim
   uint32_t abort;              // set on a fatal condition: every wait gives up
   int32_t status;              // first MOE_FFN_STATUS_* of the call
-  uint32_t pad[56];
+  uint32_t pad[53];
 };
 static_assert(sizeof(Ctrl) == 256, "control block must stay 256 bytes");
 static_assert(offsetof(Ctrl, bar) == 0, "barrier counters lead the control block");
-static_assert(offsetof(Ctrl, exit_count) == 16, "layout change must be deliberate");
-static_assert(offsetof(Ctrl, status) == 28, "layout change must be deliberate");
+static_assert(offsetof(Ctrl, exit_count) == 24, "layout change must be deliberate");
+static_assert(offsetof(Ctrl, status) == 40, "layout change must be deliberate");
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ctrl, counts, offsets, hist, r2s, s2r, ready, h, h_sf, o, total;
+  size_t ctrl, counts, offsets, hist, r2s, s2r, h, h_sf, o, total;
   int64_t chunk_slots;   // slots per routing chunk
   int64_t max_slots;     // max_tokens * k
-  int64_t ready_len;     // readiness counters (one per token block of any expert)
   int64_t h_rows;        // rows of h (max_slots + kMaxBM padding)
   int64_t h_row_bytes, h_sf_row_bytes, o_row_bytes;
 };
@@ -52,7 +53,6 @@ inline Layout make_layout(int64_t max_tokens, int64_t H, int64_t I, int64_t E, i
   int64_t per = (L.max_slots + kMaxChunks - 1) / kMaxChunks;
   L.chunk_slots = per <= kMinChunkSlots ? kMinChunkSlots
                                         : (per + kMinChunkSlots - 1) / kMinChunkSlots * kMinChunkSlots;
-  L.ready_len = (L.max_slots + kMinBM - 1) / kMinBM + E;
   L.h_rows = L.max_slots + kMaxBM;
   L.h_row_bytes = recipe == 0 ? I * 2 : I;
   L.h_sf_row_bytes = recipe == 0 ? 0 : I / 32;
@@ -64,7 +64,6 @@ inline Layout make_layout(int64_t max_tokens, int64_t H, int64_t I, int64_t E, i
   L.hist = off;    off = align_up(off + sizeof(int32_t) * (size_t)kMaxChunks * (size_t)E, A);
   L.r2s = off;     off = align_up(off + sizeof(int32_t) * (size_t)(L.max_slots + 1), A);
   L.s2r = off;     off = align_up(off + sizeof(int32_t) * (size_t)(L.max_slots + 1), A);
-  L.ready = off;   off = align_up(off + sizeof(uint32_t) * (size_t)L.ready_len, A);
   L.h = off;       off = align_up(off + (size_t)L.h_rows * (size_t)L.h_row_bytes, A);
   L.h_sf = off;    off = align_up(off + (size_t)L.h_rows * (size_t)L.h_sf_row_bytes, A);
   L.o = off;       off = align_up(off + (size_t)(L.max_slots > 0 ? L.max_slots : 1) * (size_t)L.o_row_bytes, A);

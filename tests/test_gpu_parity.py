@@ -31,7 +31,7 @@ def _small_cfg(recipe, T, H, I, E, k, routing="softmax", seed=7, y_fp32=False):
     return synth.Config(f"r{recipe}_T{T}_H{H}_I{I}_E{E}_k{k}", recipe, T, H, I, E, k, routing, seed, y_fp32=y_fp32)
 
 
-@pytest.mark.parametrize("T", [0, 8, 48, 192, 1000])
+@pytest.mark.parametrize("T", [0, 8, 48, 192, 1000, 1500])
 def test_routing_bitexact_with_masks(T):
     cfg = _small_cfg(synth.RECIPE_FP8_FP4, max(T, 1), 256, 128, 16, 4, "uniform", seed=31)
     p = synth.make_problem(cfg, T=max(T, 1), threads=4)
