@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI (no GPU needed, no compute calls).
+
+The library must load and export every function include/moe_ffn.h declares;
+the launch-size rule must follow the CU-reserve arithmetic of the sglang
+"Reserve SMs for DeepGEMM MegaMoE grid barriers" change (physical CUs minus
+the reserve, at least 2, capped, rounded down to even); argument checks must
+fail with the documented codes before touching a device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_histogram_amd as mf
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    text = open(os.path.join(ROOT, "include", "moe_ffn.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(moe_ffn_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _header_functions()
+    assert set(names) == set(mf.EXPORTS), names
+    lib = mf.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("phys,reserve,cap,expect", [
+    (256, 2, 0, 254),      # default reserve on MI355X
+    (256, 0, 0, 256),      # reserve disabled
+    (256, -3, 0, 256),     # negative reserve counts as 0
+    (256, 3, 0, 252),      # odd result rounded down to even
+    (255, 0, 0, 254),
+    (256, 256, 0, 2),      # excessive reserve keeps 2
+    (256, 1000, 0, 2),
+    (256, 2, 100, 100),    # cap below the limit
+    (256, 2, 101, 100),    # odd cap rounded down
+    (256, 2, 300, 254),    # cap above the limit has no effect
+    (256, 2, 1, 2),        # never below 2
+    (8, 2, 0, 6),
+])
+def test_launch_size_rule(phys, reserve, cap, expect):
+    assert mf.launch_size(phys, reserve, cap) == expect
+
+
+def test_workspace_size_depends_on_problem_only_and_grows_with_tokens():
+    sizes = [mf.get_workspace_size(mf.make_problem(t, 7168, 2048, 256, 8, mf.RECIPE_FP8_FP4))
+             for t in (0, 1, 128, 8192)]
+    assert sizes == sorted(sizes) and sizes[0] > 0
+    v = mf.get_workspace_view(mf.make_problem(128, 7168, 2048, 256, 8, mf.RECIPE_FP8_FP4))
+    assert v.h_row_bytes == 2048 and v.h_sf_row_bytes == 64 and v.o_row_bytes == 7168 * 4
+    assert v.h % 256 == 0 and v.h_sf % 256 == 0 and v.o % 256 == 0
+    assert v.o + 128 * 8 * 7168 * 4 <= sizes[2]
+    vb = mf.get_workspace_view(mf.make_problem(64, 256, 128, 8, 2, mf.RECIPE_BF16))
+    assert vb.h_row_bytes == 256 and vb.h_sf_row_bytes == 0
+
+
+def test_token_alignment_and_strerror():
+    for r in (mf.RECIPE_BF16, mf.RECIPE_FP8_FP8, mf.RECIPE_FP8_FP4):
+        assert mf.get_token_alignment(r) == 1
+    with pytest.raises(mf.MoeFFNError):
+        mf.get_token_alignment(7)
+    for code in (mf.OK, mf.ERR_INVALID_ARG, mf.ERR_UNSUPPORTED, mf.ERR_WORKSPACE_TOO_SMALL, mf.ERR_HIP,
+                 mf.STATUS_BAD_EXPERT_INDEX, mf.STATUS_TIMEOUT, mf.STATUS_DIRTY_WORKSPACE):
+        assert mf.strerror(code) and mf.strerror(code) != "unknown code"
+
+
+@pytest.mark.parametrize("dims,code", [
+    ((16, 100, 128, 8, 2, mf.RECIPE_FP8_FP4), mf.ERR_UNSUPPORTED),   # H not a multiple of 128
+    ((16, 256, 96, 8, 2, mf.RECIPE_FP8_FP8), mf.ERR_UNSUPPORTED),    # I not a multiple of 128
+    ((16, 256, 128, 513, 2, mf.RECIPE_FP8_FP4), mf.ERR_UNSUPPORTED),  # too many experts
+    ((16, 256, 128, 8, 65, mf.RECIPE_FP8_FP4), mf.ERR_UNSUPPORTED),   # top-k too large
+    ((-1, 256, 128, 8, 2, mf.RECIPE_FP8_FP4), mf.ERR_INVALID_ARG),
+    ((16, 256, 128, 0, 2, mf.RECIPE_FP8_FP4), mf.ERR_INVALID_ARG),
+    ((16, 256, 128, 8, 2, 3), mf.ERR_INVALID_ARG),
+])
+def test_problem_validation(dims, code):
+    with pytest.raises(mf.MoeFFNError) as ei:
+        mf.get_workspace_size(mf.make_problem(*dims))
+    assert ei.value.code == code
+
+
+def _args(**kw):
+    a = mf.Args()
+    a.num_tokens = kw.get("num_tokens", 4)
+    for n in ("x", "x_sf", "topk_idx", "topk_weights", "w1", "w1_sf", "w2", "w2_sf", "y"):
+        setattr(a, n, kw.get(n, 4096))   # aligned non-null sentinels; never dereferenced on these paths
+    a.y_dtype = kw.get("y_dtype", mf.Y_BF16)
+    a.activation_clamp = 7.0
+    a.reserved_cus = -1
+    return a
+
+
+@pytest.mark.parametrize("change,code", [
+    ({"num_tokens": 17}, mf.ERR_INVALID_ARG),          # above max_tokens
+    ({"num_tokens": -1}, mf.ERR_INVALID_ARG),
+    ({"x": None}, mf.ERR_INVALID_ARG),
+    ({"w1": 4100}, mf.ERR_INVALID_ARG),                # misaligned
+    ({"y_dtype": 5}, mf.ERR_INVALID_ARG),
+])
+def test_forward_argument_checks_fail_before_any_device_work(change, code):
+    prob = mf.make_problem(16, 256, 128, 8, 2, mf.RECIPE_FP8_FP4)
+    a = _args(**change)
+    ws = ctypes.c_void_p(1 << 20)
+    rc = mf.lib().moe_ffn_forward(ctypes.byref(prob), ctypes.byref(a), ws, ctypes.c_size_t(1 << 40), None)
+    assert rc == code
+
+
+def test_forward_rejects_small_workspace():
+    prob = mf.make_problem(16, 256, 128, 8, 2, mf.RECIPE_FP8_FP4)
+    a = _args()
+    need = mf.get_workspace_size(prob)
+    rc = mf.lib().moe_ffn_forward(ctypes.byref(prob), ctypes.byref(a), ctypes.c_void_p(1 << 20),
+                                  ctypes.c_size_t(need - 1), None)
+    assert rc == mf.ERR_WORKSPACE_TOO_SMALL
