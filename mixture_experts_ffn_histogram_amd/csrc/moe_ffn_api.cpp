@@ -188,9 +188,14 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   k.o = reinterpret_cast<float*>(ws + L.o);
 
   int bm = choose_block_m(recipe, T, p->top_k, p->num_experts);
+  // 128-row tiles address x, h and one expert's weights with 32-bit buffer offsets
+  const int64_t lim = (int64_t)1 << 31;
+  const bool big_ok = p->max_tokens * p->hidden < lim && (p->max_tokens * p->top_k + 128) * p->intermediate < lim &&
+                      p->intermediate * p->hidden < lim;
   const long bm_env = env_long("MOE_FFN_BLOCK_M", 0);  // tuning override: 16, 32, 64 or 128
   if ((bm_env == 16 || bm_env == 32 || bm_env == 64 || bm_env == 128) && bm_env <= moeffn::max_block_m(recipe))
     bm = (int)bm_env;
+  if (bm == 128 && !big_ok) bm = 64;
   if (env_long("MOE_FFN_LOG", 0) > 0)
     std::fprintf(stderr, "moe_ffn: T=%lld recipe=%d grid=%d (CUs %d, reserve %d, cap %d) block_m=%d\n",
                  (long long)T, recipe, grid, cus, reserve, a->max_cus, bm);

@@ -33,6 +33,27 @@ __device__ __forceinline__ void stg4(void* p, uint32_t v) { *(gu32*)p = v; }
 __device__ __forceinline__ void stg1(void* p, uint8_t v) { *(gu8*)p = v; }
 __device__ __forceinline__ void stg8(void* p, uint32_t lo, uint32_t hi) { *(gu64*)p = ((uint64_t)hi << 32) | lo; }
 
+// Buffer resources: a 32-bit byte range of device memory addressed by a
+// per-lane VGPR offset plus a wave-uniform SGPR offset.  Reads past the range
+// return zero.  The LDS variant writes each lane's bytes straight to LDS at
+// the wave-uniform destination + lane * size (no VGPR staging).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ v4i buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+#define MOEFFN_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+__device__ __forceinline__ void buf_load_lds16(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, MOEFFN_LDS(lds), 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buf_load_lds4(rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, MOEFFN_LDS(lds), 4, voff, soff, 0, 0);
+}
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define MOEFFN_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
 // ---------------------------------------------------------------------------
 // Number formats
 // ---------------------------------------------------------------------------

@@ -71,12 +71,16 @@ struct Shared {
   int off[kMaxExperts + 1];     // expert row offsets
   int mbo[kMaxExperts + 1];     // expert token-block offsets
   int cnt[kMaxExperts];         // expert counts / histogram scratch
-  int wcnt[4][kMaxExperts];     // per-wave running counters of the scatter
-  int r2s[kLocalRouteSlots];    // row -> slot of a small call (routed in LDS)
   int scan[4];
   int flag;
   uint32_t tile;
 };
+
+// Routing scratch in LDS: per-wave running counters of the scatter and, for a
+// small call, the row -> slot table of the whole call.  The 128-row tile
+// kernel keeps the counters inside its first ring buffer and has no table
+// (its calls always route through the workspace).
+typedef int WaveCounters[4][kMaxExperts];
 
 template <int BM>
 struct SharedB {
@@ -87,8 +91,8 @@ struct SharedB {
 };
 
 // Slot of routed row `row`: from LDS for a small call, else from the workspace.
-__device__ __forceinline__ int route_slot(const KParams& p, const Shared& sh, bool local, int row) {
-  return local ? sh.r2s[row] : (int)ldg4(p.r2s + row);
+__device__ __forceinline__ int route_slot(const KParams& p, const int* lr2s, bool local, int row) {
+  return local ? lr2s[row] : (int)ldg4(p.r2s + row);
 }
 
 // ---------------------------------------------------------------------------
@@ -180,12 +184,12 @@ __device__ void table_scan(const int* src, int* dst, int E, Shared& sh) {
 }
 
 // Row offsets and token-block offsets of the experts from sh.cnt.
-__device__ void build_tables(const KParams& p, Shared& sh, int bm) {
+__device__ void build_tables(const KParams& p, Shared& sh, WaveCounters& wcnt, int bm) {
   const int tid = threadIdx.x;
   table_scan(sh.cnt, sh.off, p.E, sh);
-  for (int e = tid; e < p.E; e += kThreads) sh.wcnt[0][e] = (sh.cnt[e] + bm - 1) / bm;
+  for (int e = tid; e < p.E; e += kThreads) wcnt[0][e] = (sh.cnt[e] + bm - 1) / bm;
   __syncthreads();
-  table_scan(sh.wcnt[0], sh.mbo, p.E, sh);
+  table_scan(wcnt[0], sh.mbo, p.E, sh);
 }
 
 // Counts and offsets to the workspace and the optional outputs.
@@ -207,8 +211,8 @@ __device__ void publish_tables(const KParams& p, const Shared& sh) {
 // LDS.  The first row of expert e in this range is off[e] + (prefix ? prefix[e] : 0).
 // Rows go to the LDS table `lds_r2s` and/or, when `to_global`, to the
 // workspace and the optional outputs.
-__device__ void scatter_range(const KParams& p, Shared& sh, int beg, int end, const int* prefix, int* lds_r2s,
-                              bool to_global) {
+__device__ void scatter_range(const KParams& p, Shared& sh, WaveCounters& wcnt, int beg, int end, const int* prefix,
+                              int* lds_r2s, bool to_global) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = p.E;
   const int NB = E > 1 ? 32 - __clz(E - 1) : 0;
@@ -216,7 +220,7 @@ __device__ void scatter_range(const KParams& p, Shared& sh, int beg, int end, co
   const int quarter = ((end - beg + 3) / 4 + 63) / 64 * 64;
   const int wbeg = beg + wave * quarter;
   const int wend = min(end, wbeg + quarter);
-  for (int e = lane; e < E; e += 64) sh.wcnt[wave][e] = 0;
+  for (int e = lane; e < E; e += 64) wcnt[wave][e] = 0;
   __syncthreads();
   for (int s0 = wbeg; s0 < wend; s0 += 64) {
     const int s = s0 + lane;
@@ -229,14 +233,14 @@ __device__ void scatter_range(const KParams& p, Shared& sh, int beg, int end, co
       const uint64_t bb = __ballot(valid && bit);
       m &= bit ? bb : ~bb;
     }
-    if (valid && __popcll(m & lt) == 0) sh.wcnt[wave][e] += __popcll(m);
+    if (valid && __popcll(m & lt) == 0) wcnt[wave][e] += __popcll(m);
   }
   __syncthreads();
   for (int e = tid; e < E; e += kThreads) {
     int run = sh.off[e] + (prefix ? prefix[e] : 0);
     for (int w = 0; w < 4; w++) {
-      const int t = sh.wcnt[w][e];
-      sh.wcnt[w][e] = run;
+      const int t = wcnt[w][e];
+      wcnt[w][e] = run;
       run += t;
     }
   }
@@ -254,8 +258,8 @@ __device__ void scatter_range(const KParams& p, Shared& sh, int beg, int end, co
       m &= bit ? bb : ~bb;
     }
     const int rank = __popcll(m & lt);
-    const int base = valid ? sh.wcnt[wave][e] : 0;
-    if (valid && rank == 0) sh.wcnt[wave][e] = base + __popcll(m);
+    const int base = valid ? wcnt[wave][e] : 0;
+    if (valid && rank == 0) wcnt[wave][e] = base + __popcll(m);
     if (valid) {
       const int row = base + rank;
       if (lds_r2s) lds_r2s[row] = s;
@@ -275,7 +279,7 @@ __device__ void scatter_range(const KParams& p, Shared& sh, int beg, int end, co
 
 // Small call: every workgroup routes the whole call in LDS; workgroup 0
 // publishes the tables (read by the combine after later barriers).
-__device__ void phase_route_local(const KParams& p, Shared& sh, int S, int bm) {
+__device__ void phase_route_local(const KParams& p, Shared& sh, WaveCounters& wcnt, int* lr2s, int S, int bm) {
   const int tid = threadIdx.x;
   for (int e = tid; e < p.E; e += kThreads) sh.cnt[e] = 0;
   __syncthreads();
@@ -287,21 +291,21 @@ __device__ void phase_route_local(const KParams& p, Shared& sh, int S, int bm) {
   }
   __syncthreads();
   if (bad && blockIdx.x == 0) raise_status(p, ST_BAD_EXPERT_INDEX, false);
-  build_tables(p, sh, bm);
+  build_tables(p, sh, wcnt, bm);
   if (blockIdx.x == 0) publish_tables(p, sh);
-  scatter_range(p, sh, 0, S, nullptr, sh.r2s, blockIdx.x == 0);
+  scatter_range(p, sh, wcnt, 0, S, nullptr, lr2s, blockIdx.x == 0);
 }
 
 // Large call, R3: tables from the column scan, then the chunk scatter.
-__device__ void phase_scatter_global(const KParams& p, Shared& sh, int S, int C, int bm) {
+__device__ void phase_scatter_global(const KParams& p, Shared& sh, WaveCounters& wcnt, int S, int C, int bm) {
   const int tid = threadIdx.x;
   for (int e = tid; e < p.E; e += kThreads) sh.cnt[e] = p.counts[e];
   __syncthreads();
-  build_tables(p, sh, bm);
+  build_tables(p, sh, wcnt, bm);
   if (blockIdx.x == 0) publish_tables(p, sh);
   for (int c = blockIdx.x; c < C; c += gridDim.x) {
     const int beg = c * (int)p.chunk_slots;
-    scatter_range(p, sh, beg, min(S, beg + (int)p.chunk_slots), p.hist + (size_t)c * p.E, nullptr, true);
+    scatter_range(p, sh, wcnt, beg, min(S, beg + (int)p.chunk_slots), p.hist + (size_t)c * p.E, nullptr, true);
   }
 }
 
@@ -329,7 +333,8 @@ __device__ __forceinline__ int find_expert(const int* mbo, int E, int nb, int t)
 // L1: 4 waves x (32 gate + 32 up rows) = 128 intermediate features;
 // L2: 4 waves x 64 rows = 256 hidden outputs.
 template <int RECIPE, int BM>
-__device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, bool local, bool l1, int e, int mb, int nb) {
+__device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const int* lr2s, bool local, bool l1, int e, int mb,
+                          int nb) {
   using C = Cfg<RECIPE, BM>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const int H = p.H, I = p.I;
@@ -346,7 +351,7 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, bool lo
   if (tid < BM) {
     const int m = tid;
     if (l1) {
-      const uint32_t tok = (uint32_t)(route_slot(p, sh, local, row0 + (m < nrows ? m : 0)) / p.k);
+      const uint32_t tok = (uint32_t)(route_slot(p, lr2s, local, row0 + (m < nrows ? m : 0)) / p.k);
       sb.boff[m] = tok * (uint32_t)H * (C::kBF16 ? 2u : 1u);
       sb.bsfoff[m] = tok * (uint32_t)(H / 32);
     } else {
@@ -575,7 +580,7 @@ struct WCfg {
 };
 
 template <int RECIPE, int BM>
-__device__ void wave_tile(const KParams& p, const Shared& sh, bool local, bool l1, int e, int mb, int blk) {
+__device__ void wave_tile(const KParams& p, const Shared& sh, const int* lr2s, bool local, bool l1, int e, int mb, int blk) {
   using C = WCfg<RECIPE, BM>;
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const int H = p.H, I = p.I;
@@ -616,7 +621,7 @@ __device__ void wave_tile(const KParams& p, const Shared& sh, bool local, bool l
   for (int t = 0; t < C::NTB; t++) {
     const int m = t * 16 + r16;
     if (l1) {
-      const uint32_t tok = (uint32_t)(route_slot(p, sh, local, row0 + (m < nrows ? m : 0)) / p.k);
+      const uint32_t tok = (uint32_t)(route_slot(p, lr2s, local, row0 + (m < nrows ? m : 0)) / p.k);
       boff[t] = tok * (uint32_t)H * (C::kBF16 ? 2u : 1u);
       bsfoff[t] = tok * (uint32_t)(H / 32);
     } else {
@@ -766,6 +771,231 @@ __device__ void wave_tile(const KParams& p, const Shared& sh, bool local, bool l
   }
 }
 
+// ---------------------------------------------------------------------------
+// 128-row workgroup tiles for e4m3 rows x e2m1 weights (the MFMA-bound
+// regime).  4 waves x 64 weight rows x 128 routed rows, acc[j][t] for weight
+// row block j and routed-row block t.  Each wave streams its own weight rows
+// into a register ring kBigP stages deep.  The routed rows and the 1x32
+// scales of both operands go through a kBigNB-deep LDS ring filled by buffer
+// loads that write LDS directly, kBigD stages ahead; one workgroup barrier per
+// 128-element K stage publishes a stage to every wave.  Waits on the ring are
+// explicit: with the issue order pinned (scheduling barriers), the fill of
+// stage s is complete once at most kBigWait younger vector-memory operations
+// are outstanding.  Each ring buffer is its own LDS object, so the compiler's
+// own wait for a DMA'd buffer only covers the fills of that buffer.
+// ---------------------------------------------------------------------------
+constexpr int kBigBM = 128, kBigNB = 3, kBigD = 2, kBigP = 3;
+constexpr int kBigBsf = kBigBM * 128;               // routed-row scale dwords (+ a second copy)
+constexpr int kBigAsf = kBigBsf + 2 * kBigBM * 4;   // weight-row scale dwords
+constexpr int kBigBuf = kBigAsf + 256 * 4;          // 18432 bytes per stage
+constexpr int kBigWait = 4 + 10 * (kBigD - 1);      // younger VMEM ops allowed when stage s is consumed
+static_assert(kBigP == kBigNB && kBigD == kBigNB - 1, "ring indices assume P = NB = D + 1");
+
+struct BigRing {
+  uint8_t* b0;
+  uint8_t* b1;
+  uint8_t* b2;
+};
+
+__device__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __restrict__ B1, uint8_t* __restrict__ B2,
+                          v4f (&acc)[4][8], rsrc_t rW, uint32_t a_off, const uint32_t (&a_soff)[4], rsrc_t rWs,
+                          uint32_t as_off, rsrc_t rX, uint32_t xa_off, uint32_t xb_off, rsrc_t rXs,
+                          uint32_t xs_off, int nk, int wave, int lane) {
+  const int g = lane >> 4, r16 = lane & 15;
+  auto BUF = [&](int u) -> uint8_t* { return u == 0 ? B0 : u == 1 ? B1 : B2; };
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int t = 0; t < 8; t++) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4i ar[kBigP][4];
+
+  auto load_a = [&](int slot, int s) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) ar[slot][j] = buf_load16(rW, a_off, a_soff[j] + (uint32_t)s * 64);
+  };
+  // Stage s into ring buffer `buf`: 16 x 1 KB of routed-row bytes (piece
+  // (t, half) holds bytes half*64 + g*16 .. +16 of row t*16 + c at lane
+  // g*16 + c: the e4m3 MFMA operand layout), the routed-row scale dwords
+  // (waves 2-3 write a second copy so every wave issues the same count) and
+  // the weight-row scale dwords of the wave's 64 rows.
+  auto dma = [&](int s, int buf) {
+    uint8_t* bp = BUF(buf);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      buf_load_lds16(rX, bp + (wave * 4 + i) * 1024, (i >> 1) ? xb_off : xa_off, (uint32_t)s * 128 + (i & 1) * 64);
+    buf_load_lds4(rXs, bp + kBigBsf + ((wave >> 1) * kBigBM + (wave & 1) * 64) * 4, xs_off, (uint32_t)s * 4);
+    buf_load_lds4(rWs, bp + kBigAsf + wave * 64 * 4, as_off, (uint32_t)s * 4);
+  };
+  auto compute = [&](int slot, int buf) {
+    const uint8_t* bp = BUF(buf);
+    int sa[4], sb[8];
+#pragma unroll
+    for (int j = 0; j < 4; j++) sa[j] = bp[kBigAsf + (wave * 64 + j * 16 + r16) * 4 + g];
+#pragma unroll
+    for (int t = 0; t < 8; t++) sb[t] = bp[kBigBsf + (t * 16 + r16) * 4 + g];
+    v4i n0 = *(const v4i*)(bp + (0 * 64 + lane) * 16);
+    v4i n1 = *(const v4i*)(bp + (1 * 64 + lane) * 16);
+    __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const v8i bb = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3]};
+      if (t < 7) {
+        n0 = *(const v4i*)(bp + (((t + 1) * 2) * 64 + lane) * 16);
+        n1 = *(const v4i*)(bp + (((t + 1) * 2 + 1) * 64 + lane) * 16);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const v8i aa = {ar[slot][j][0], ar[slot][j][1], ar[slot][j][2], ar[slot][j][3], 0, 0, 0, 0};
+        acc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, acc[j][t], 4, 0, 0, sa[j], 0, sb[t]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
+  };
+
+  // Earlier stores and loads of this wave must not be counted as ring fills.
+  MOEFFN_WAIT_VMCNT(0);
+  // Prologue, in the steady issue order: virtual iterations -P..-1 each issue
+  // the fill of stage it + D, then the weight loads of stage it + P.
+  load_a(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_a(1, 1 < nk ? 1 : nk - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(1 < nk ? 1 : nk - 1, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  load_a(2, 2 < nk ? 2 : nk - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  int s0 = 0;
+  for (; s0 + kBigP <= nk; s0 += kBigP) {
+#pragma unroll
+    for (int u = 0; u < kBigP; u++) {
+      const int s = s0 + u;
+      MOEFFN_WAIT_VMCNT(kBigWait);        // this wave's fill of stage s has landed
+      __builtin_amdgcn_s_barrier();       // ... and every other wave's
+      dma(s + kBigD < nk ? s + kBigD : nk - 1, (u + kBigD) % kBigNB);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(u, u);
+      load_a(u, s + kBigP < nk ? s + kBigP : nk - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // nk % P trailing stages: already in flight in buffer / slot u
+#pragma unroll
+  for (int u = 0; u < kBigP - 1; u++) {
+    if (s0 + u < nk) {
+      MOEFFN_WAIT_VMCNT(0);
+      __builtin_amdgcn_s_barrier();
+      compute(u, u);
+    }
+  }
+  // every wave is done with the ring before the next tile refills it
+  MOEFFN_WAIT_VMCNT(0);
+  __builtin_amdgcn_s_barrier();
+}
+
+// One 128-row tile: expert e, token block mb, feature block nb (L1: 128
+// intermediate features = 4 waves x (32 gate + 32 up rows); L2: 256 hidden
+// outputs = 4 waves x 64 rows).
+template <int RECIPE>
+__device__ void big_tile(const KParams& p, const Shared& sh, const BigRing& R, bool l1, int e, int mb, int nb) {
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
+  const int H = p.H, I = p.I;
+  const int row0 = __builtin_amdgcn_readfirstlane(sh.off[e] + mb * kBigBM);
+  const int nrows = __builtin_amdgcn_readfirstlane(min(kBigBM, sh.cnt[e] - mb * kBigBM));
+  const int K = l1 ? H : I;
+  const int nk = K / 128;
+  const uint32_t arow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
+  const uint32_t wrows = l1 ? 2u * (uint32_t)I : (uint32_t)H;
+  const uint8_t* W = l1 ? p.w1 + (size_t)e * wrows * arow : p.w2 + (size_t)e * wrows * arow;
+  const uint8_t* Ws = l1 ? p.w1_sf + (size_t)e * wrows * srow : p.w2_sf + (size_t)e * wrows * srow;
+  int rb[4];  // first weight row of each 16-row block of this wave
+  if (l1) {
+    const int i0 = nb * 128 + wave * 32;
+    rb[0] = i0; rb[1] = i0 + 16; rb[2] = I + i0; rb[3] = I + i0 + 16;
+  } else {
+    const int n0 = nb * 256 + wave * 64;  // rows past H (last block of an odd H/128) read as zero
+    rb[0] = n0; rb[1] = n0 + 16; rb[2] = n0 + 32; rb[3] = n0 + 48;
+  }
+  const bool active = l1 || rb[0] < H;
+  uint32_t a_soff[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) a_soff[j] = (uint32_t)rb[j] * arow;
+  const rsrc_t rW = make_rsrc(W, wrows * arow);
+  const rsrc_t rWs = make_rsrc(Ws, wrows * srow);
+  const uint32_t a_off = (uint32_t)r16 * arow + (uint32_t)g * 16;
+  const uint32_t as_off = (uint32_t)(rb[lane >> 4] + r16) * srow;
+
+  // routed rows of the tile (rows past the expert repeat its first row / read padding)
+  const int c = r16;
+  const int ma = (wave * 2) * 16 + c, mbb = (wave * 2 + 1) * 16 + c, ms = (wave & 1) * 64 + lane;
+  rsrc_t rX, rXs;
+  uint32_t xa_off, xb_off, xs_off;
+  if (l1) {
+    const uint32_t ta = (uint32_t)(route_slot(p, nullptr, false, row0 + (ma < nrows ? ma : 0)) / p.k);
+    const uint32_t tb = (uint32_t)(route_slot(p, nullptr, false, row0 + (mbb < nrows ? mbb : 0)) / p.k);
+    const uint32_t ts = (uint32_t)(route_slot(p, nullptr, false, row0 + (ms < nrows ? ms : 0)) / p.k);
+    rX = make_rsrc(p.x, (uint32_t)p.T * (uint32_t)H);
+    rXs = make_rsrc(p.x_sf, (uint32_t)p.T * (uint32_t)(H / 32));
+    xa_off = ta * (uint32_t)H + (uint32_t)g * 16;
+    xb_off = tb * (uint32_t)H + (uint32_t)g * 16;
+    xs_off = ts * (uint32_t)(H / 32);
+  } else {
+    const uint32_t rows_end = (uint32_t)(row0 + kBigBM);  // h is padded by kMaxBM rows
+    rX = make_rsrc(p.h, rows_end * (uint32_t)I);
+    rXs = make_rsrc(p.h_sf, rows_end * (uint32_t)(I / 32));
+    xa_off = (uint32_t)(row0 + ma) * (uint32_t)I + (uint32_t)g * 16;
+    xb_off = (uint32_t)(row0 + mbb) * (uint32_t)I + (uint32_t)g * 16;
+    xs_off = (uint32_t)(row0 + ms) * (uint32_t)(I / 32);
+  }
+
+  v4f acc[4][8];
+  big_kloop(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, rX, xa_off, xb_off, rXs, xs_off, nk, wave, lane);
+
+  if (!active) return;
+  if (l1) {
+    const int i0 = rb[0];
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const int m = t * 16 + r16;
+      float hv[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp);
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const int E = block_scale_exp(amax);
+      if (m < nrows) {
+        const size_t row = (size_t)(row0 + m);
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int j = 0; j < 4; j++) word |= f32_to_e4m3(__builtin_amdgcn_ldexpf(hv[hh * 4 + j], -E)) << (8 * j);
+          stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
+        }
+        if (g == 0) stg1(p.h_sf + row * (size_t)(I / 32) + (size_t)(i0 / 32), (uint8_t)(E + 127));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+      const int m = t * 16 + r16;
+      if (m < nrows) {
+        const size_t row = (size_t)(row0 + m);
+#pragma unroll
+        for (int j = 0; j < 4; j++) stg16f(p.o + row * H + (size_t)(rb[j] + 4 * g), acc[j][t]);
+      }
+    }
+  }
+}
+
 
 // Tile queues.  Tile ids run over (expert, feature block, token block), token
 // block fastest, so tiles claimed together share a weight slice.
@@ -781,7 +1011,7 @@ __device__ __forceinline__ void decode_tile(const Shared& sh, int E, int NB, int
 // for the next tile is issued before the current tile starts, so its round
 // trip overlaps the tile's loads.
 template <int RECIPE, int BM>
-__device__ void phase_wave_tiles(const KParams& p, Shared& sh, bool local, bool l1) {
+__device__ void phase_wave_tiles(const KParams& p, Shared& sh, const int* lr2s, bool local, bool l1) {
   const int lane = threadIdx.x & 63;
   const int E = p.E;
   const int NB = l1 ? p.I / 32 : p.H / 64;
@@ -795,13 +1025,13 @@ __device__ void phase_wave_tiles(const KParams& p, Shared& sh, bool local, bool 
     if (lane == 0) next = __hip_atomic_fetch_add(q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int e, mb, blk;
     decode_tile(sh, E, NB, (int)t, e, mb, blk);
-    wave_tile<RECIPE, BM>(p, sh, local, l1, e, mb, blk);
+    wave_tile<RECIPE, BM>(p, sh, lr2s, local, l1, e, mb, blk);
   }
 }
 
 // Workgroup-tile phase (token blocks of 64/128).
 template <int RECIPE, int BM>
-__device__ void phase_wg_tiles(const KParams& p, Shared& sh, SharedB<BM>& sb, bool local, bool l1) {
+__device__ void phase_wg_tiles(const KParams& p, Shared& sh, SharedB<BM>& sb, const int* lr2s, bool local, bool l1) {
   const int tid = threadIdx.x;
   const int E = p.E;
   const int NB = l1 ? (p.I + 127) / 128 : (p.H + 255) / 256;
@@ -818,7 +1048,31 @@ __device__ void phase_wg_tiles(const KParams& p, Shared& sh, SharedB<BM>& sb, bo
     if (tid == 0) next = __hip_atomic_fetch_add(q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int e, mb, nb;
     decode_tile(sh, E, NB, (int)t, e, mb, nb);
-    gemm_tile<RECIPE, BM>(p, sh, sb, local, l1, e, mb, nb);
+    gemm_tile<RECIPE, BM>(p, sh, sb, lr2s, local, l1, e, mb, nb);
+  }
+}
+
+// 128-row tile phase (same queue order as the workgroup tiles).
+template <int RECIPE>
+__device__ void phase_big_tiles(const KParams& p, Shared& sh, const BigRing& R, bool l1) {
+  const int tid = threadIdx.x;
+  const int E = p.E;
+  const int NB = l1 ? p.I / 128 : (p.H + 255) / 256;
+  const uint32_t n = (uint32_t)(sh.mbo[E] * NB);
+  uint32_t* q = l1 ? &p.ctrl->tile_next : &p.ctrl->tile_next2;
+  uint32_t next = 0;
+  if (tid == 0) next = __hip_atomic_fetch_add(q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    if (tid == 0) sh.tile = next;
+    __syncthreads();
+    const uint32_t t = __builtin_amdgcn_readfirstlane(sh.tile);
+    __syncthreads();
+    if (t >= n) break;
+    if (tid == 0) next = __hip_atomic_fetch_add(q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int e, mb, nb;
+    decode_tile(sh, E, NB, (int)t, e, mb, nb);
+    big_tile<RECIPE>(p, sh, R, l1, __builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(mb),
+                     __builtin_amdgcn_readfirstlane(nb));
   }
 }
 
@@ -884,12 +1138,12 @@ __device__ void phase_combine(const KParams& p) {
 // another stream holds a few CUs of an XCD.
 // ---------------------------------------------------------------------------
 template <int RECIPE, int BM>
-__global__ __launch_bounds__(kThreads, 2) void moe_ffn_kernel(KParams p) {
-  __shared__ Shared sh;
-  __shared__ SharedB<(BM > 32 ? BM : 16)> sb;
+__device__ __forceinline__ void run_call(const KParams& p, Shared& sh, WaveCounters& wcnt, int* lr2s,
+                                         SharedB<(BM > 32 && BM < 128 ? BM : 16)>* sb, const BigRing* big) {
+  constexpr bool kBig = RECIPE == 2 && BM == kBigBM;
   const int tid = threadIdx.x;
   const int S = p.T * p.k;
-  const bool local = S <= kLocalRouteSlots;
+  const bool local = !kBig && S <= kLocalRouteSlots;
 
   if (tid == 0) {
     int dirty = 0;
@@ -906,21 +1160,23 @@ __global__ __launch_bounds__(kThreads, 2) void moe_ffn_kernel(KParams p) {
 
   if (!dirty) {
     if (local) {
-      phase_route_local(p, sh, S, BM);
+      phase_route_local(p, sh, wcnt, lr2s, S, BM);
     } else {
       const int C = (S + (int)p.chunk_slots - 1) / (int)p.chunk_slots;
       phase_histogram(p, sh, S, C);
       if (!grid_barrier(p, BAR_HIST, sh)) goto done;
       phase_column_scan(p, sh, C);
       if (!grid_barrier(p, BAR_COLSCAN, sh)) goto done;
-      phase_scatter_global(p, sh, S, C, BM);
+      phase_scatter_global(p, sh, wcnt, S, C, BM);
       if (!grid_barrier(p, BAR_SCATTER, sh)) goto done;
     }
-    if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM>(p, sh, local, true);
-    else phase_wg_tiles<RECIPE, BM>(p, sh, sb, local, true);
+    if constexpr (kBig) phase_big_tiles<RECIPE>(p, sh, *big, true);
+    else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM>(p, sh, lr2s, local, true);
+    else phase_wg_tiles<RECIPE, BM>(p, sh, *sb, lr2s, local, true);
     if (!grid_barrier(p, BAR_L1, sh)) goto done;
-    if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM>(p, sh, local, false);
-    else phase_wg_tiles<RECIPE, BM>(p, sh, sb, local, false);
+    if constexpr (kBig) phase_big_tiles<RECIPE>(p, sh, *big, false);
+    else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM>(p, sh, lr2s, local, false);
+    else phase_wg_tiles<RECIPE, BM>(p, sh, *sb, lr2s, local, false);
     if (!grid_barrier(p, BAR_L2, sh)) goto done;
     phase_combine(p);
   }
@@ -940,6 +1196,26 @@ done:
       __hip_atomic_store(&p.ctrl->status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       st_release(&p.ctrl->exit_count, 0u);
     }
+  }
+}
+
+template <int RECIPE, int BM>
+__global__ __launch_bounds__(kThreads, 2) void moe_ffn_kernel(KParams p) {
+  __shared__ Shared sh;
+  if constexpr (RECIPE == 2 && BM == kBigBM) {
+    // three ring buffers, each its own LDS object; the scatter counters of
+    // the routing phase live in the first one (routing ends before any tile)
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kBigBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t ring1[kBigBuf];
+    __shared__ __attribute__((aligned(16))) uint8_t ring2[kBigBuf];
+    static_assert(sizeof(WaveCounters) <= kBigBuf, "scatter counters must fit a ring buffer");
+    const BigRing R{ring0, ring1, ring2};
+    run_call<RECIPE, BM>(p, sh, *reinterpret_cast<WaveCounters*>(ring0), nullptr, nullptr, &R);
+  } else {
+    __shared__ WaveCounters wcnt;
+    __shared__ int lr2s[kLocalRouteSlots];
+    __shared__ SharedB<(BM > 32 && BM < 128 ? BM : 16)> sb;
+    run_call<RECIPE, BM>(p, sh, wcnt, lr2s, &sb, nullptr);
   }
 }
 

@@ -128,10 +128,22 @@ def tol_for(recipe: int) -> float:
 RHO = 2.0 ** -12
 
 
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of the bf16 grid at |v| (8 significant bits; subnormal floor 2^-133)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.ldexp(1.0, (np.maximum(e, -126) - 7).astype(np.int32)), np.ldexp(1.0, -133))
+
+
 def oracle_y_band(p: dict, y_fp32: bool, clamp: float, tokens=None):
+    """Oracle y and the per-element allowance: the re-quantisation band and,
+    for a bf16 y, one bf16 step at the value (the kernel's fp32 sum and the
+    exact one may straddle a bf16 rounding midpoint)."""
     toks = list(range(p["T"])) if tokens is None else list(tokens)
     y, allow, _ = oracle.forward_tokens_band(p, toks, y_fp32, clamp, RHO)
     yf = y.astype(np.float64) if y_fp32 else oracle.bf16_bits_to_f32(y).astype(np.float64)
+    if not y_fp32:
+        allow = allow + bf16_ulp(yf)
     return yf, allow
 
 

@@ -103,6 +103,27 @@ def test_fp8xfp4_reduced_full(T, E, k):
     log(f"  near-tie code flips in sampled rows: {flips}")
 
 
+@pytest.mark.parametrize("T,H,I,E,k", [
+    (300, 384, 128, 4, 2),    # K stages: L1 3, L2 1 (no steady loop); odd H/128: half-empty last L2 block
+    (257, 1152, 640, 2, 1),   # L1 9 stages, L2 5 (two trailing stages); ragged last token block
+    (520, 1024, 512, 3, 3),   # several full 128-row blocks per expert
+])
+def test_fp8xfp4_block128_shapes(T, H, I, E, k, monkeypatch):
+    monkeypatch.setenv("MOE_FFN_BLOCK_M", "128")
+    cfg = _small_cfg(synth.RECIPE_FP8_FP4, T, H, I, E, k, "softmax", seed=T + H)
+    p = synth.make_problem(cfg, threads=8)
+    log(f"block 128: T={T} H={H} I={I} E={E} k={k}")
+    run = Runner(p)
+    run.run()
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    _check_tables(run, p, T)
+    ref, allow = oracle_y_band(p, False, p["clamp"])
+    assert_y_parity(run.y_float(), ref, allow, 2e-2, f"block 128 T={T}")
+    R = int(run.offsets[-1].item())
+    assert_h_decisions(run, p, list(range(0, R, max(1, R // 30))) + [R - 1], p["clamp"])
+
+
 def test_deepseek_T128_sampled():
     cfg = synth.CONFIGS["deepseek_fp8xfp4_T128"]
     p = synth.make_problem(cfg, threads=16)
