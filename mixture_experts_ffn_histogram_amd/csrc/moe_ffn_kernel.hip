@@ -996,6 +996,212 @@ __device__ void big_tile(const KParams& p, const Shared& sh, const BigRing& R, b
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wave tiles of the e2m1 x e4m3 recipe with whole-cache-line loads.  A load
+// instruction that covers 16 rows x 64 bytes (half of each 128-byte line)
+// moves about half as many bytes per cycle through the vector L1 as one that
+// covers 8 rows x 128 bytes, so every load here takes whole lines: a weight
+// load brings two K stages of 8 weight rows, a routed-row load one K stage of
+// 8 rows.  In load half i (rows 8i..8i+7 of a 16-row block) lane l holds row
+// 8i + (l%16)%8, 16-byte chunk 4*((l%16)/8) + l/16 of the 128 bytes; a DPP
+// rotate by 8 lanes inside each 16-lane row plus a select rebuilds the MFMA
+// operand layout (for the weights: stage 2m from chunks 0-3, stage 2m+1 from
+// chunks 4-7; for the e4m3 rows: operand bytes 0-15 from chunks 0-3, bytes
+// 16-31 from chunks 4-7).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int dpp_ror8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
+
+// lanes 0-7 of each 16-lane row take x0 (par 0) / rotated x0 (par 1); lanes 8-15 rotated x1 / x1
+__device__ __forceinline__ v4i line_shuffle(const v4i& x0, const v4i& x1, int par, bool lo) {
+  v4i r;
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    const int rot = dpp_ror8(par == 0 ? x1[d] : x0[d]);  // every lane executes the DPP move
+    r[d] = par == 0 ? (lo ? x0[d] : rot) : (lo ? rot : x1[d]);
+  }
+  return r;
+}
+
+template <int BM>
+__device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s, bool local, bool l1, int e, int mb,
+                             int blk) {
+  constexpr int NTB = BM / 16;
+  constexpr int PP = 2;  // weight pairs (2 K stages each) in flight
+  const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
+  const bool lo = r16 < 8;
+  const int H = p.H, I = p.I;
+  const int row0 = sh.off[e] + mb * BM;
+  const int nrows = min(BM, sh.cnt[e] - mb * BM);
+  const int K = l1 ? H : I;
+  const int nk = K / 128;
+  const int npairs = (nk + 1) / 2;
+  const uint32_t arow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
+  const uint32_t wrows = l1 ? 2u * (uint32_t)I : (uint32_t)H;
+  const uint8_t* W = l1 ? p.w1 + (size_t)e * wrows * arow : p.w2 + (size_t)e * wrows * arow;
+  const uint8_t* Ws = l1 ? p.w1_sf + (size_t)e * wrows * srow : p.w2_sf + (size_t)e * wrows * srow;
+  int rb[4];
+  if (l1) {
+    const int i0 = blk * 32;
+    rb[0] = i0; rb[1] = i0 + 16; rb[2] = I + i0; rb[3] = I + i0 + 16;
+  } else {
+    const int n0 = blk * 64;
+    rb[0] = n0; rb[1] = n0 + 16; rb[2] = n0 + 32; rb[3] = n0 + 48;
+  }
+  const rsrc_t rW = make_rsrc(W, wrows * arow);
+  const rsrc_t rWs = make_rsrc(Ws, wrows * srow);
+  const uint32_t a_voff = (uint32_t)(r16 & 7) * arow + (uint32_t)(4 * (r16 >> 3) + g) * 16;
+  const uint32_t as_voff = (uint32_t)r16 * srow;
+
+  // routed rows: load half i of token block t covers tile rows t*16 + 8i .. +7
+  rsrc_t rB, rBs;
+  uint32_t b_voff[NTB][2], bs_voff[NTB];
+  const uint32_t bq = (uint32_t)(4 * (r16 >> 3) + g) * 16;
+  if (l1) {
+    rB = make_rsrc(p.x, (uint32_t)p.T * (uint32_t)H);
+    rBs = make_rsrc(p.x_sf, (uint32_t)p.T * (uint32_t)(H / 32));
+#pragma unroll
+    for (int t = 0; t < NTB; t++) {
+#pragma unroll
+      for (int i = 0; i < 2; i++) {
+        const int m = t * 16 + 8 * i + (r16 & 7);
+        const uint32_t tok = (uint32_t)(route_slot(p, lr2s, local, row0 + (m < nrows ? m : 0)) / p.k);
+        b_voff[t][i] = tok * (uint32_t)H + bq;
+      }
+      const int m = t * 16 + r16;
+      const uint32_t tok = (uint32_t)(route_slot(p, lr2s, local, row0 + (m < nrows ? m : 0)) / p.k);
+      bs_voff[t] = tok * (uint32_t)(H / 32);
+    }
+  } else {
+    const uint32_t rows_end = (uint32_t)(row0 + BM);  // h is padded by kMaxBM rows
+    rB = make_rsrc(p.h, rows_end * (uint32_t)I);
+    rBs = make_rsrc(p.h_sf, rows_end * (uint32_t)(I / 32));
+#pragma unroll
+    for (int t = 0; t < NTB; t++) {
+#pragma unroll
+      for (int i = 0; i < 2; i++) b_voff[t][i] = (uint32_t)(row0 + t * 16 + 8 * i + (r16 & 7)) * (uint32_t)I + bq;
+      bs_voff[t] = (uint32_t)(row0 + t * 16 + r16) * (uint32_t)(I / 32);
+    }
+  }
+
+  v4f acc[4][NTB];
+#pragma unroll
+  for (int j = 0; j < 4; j++)
+#pragma unroll
+    for (int t = 0; t < NTB; t++) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  v4i ar[PP][4][2];          // weight pair: row block j, load half i
+  uint32_t sar[PP][4][2];    // weight scale dwords of the pair's two stages
+  v4i br[PP][NTB][2][2];     // routed rows: block t, stage (0/1 of the pair), load half i
+  uint32_t sbr[PP][NTB][2];  // routed-row scale dwords
+
+  auto load = [&](int slot, int m) {
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+#pragma unroll
+      for (int i = 0; i < 2; i++) ar[slot][j][i] = buf_load16(rW, a_voff, (uint32_t)(rb[j] + 8 * i) * arow + (uint32_t)m * 128);
+      const uint2 sv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rWs, as_voff, (uint32_t)rb[j] * srow + (uint32_t)m * 8, 0));
+      sar[slot][j][0] = sv.x;
+      sar[slot][j][1] = sv.y;
+    }
+#pragma unroll
+    for (int t = 0; t < NTB; t++) {
+#pragma unroll
+      for (int st = 0; st < 2; st++)
+#pragma unroll
+        for (int i = 0; i < 2; i++) br[slot][t][st][i] = buf_load16(rB, b_voff[t][i], (uint32_t)(2 * m + st) * 128);
+      const uint2 sv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rBs, bs_voff[t], (uint32_t)m * 8, 0));
+      sbr[slot][t][0] = sv.x;
+      sbr[slot][t][1] = sv.y;
+    }
+  };
+  auto compute = [&](int slot, int par) {
+    v4i a[4];
+    int sa[4];
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      a[j] = line_shuffle(ar[slot][j][0], ar[slot][j][1], par, lo);
+      sa[j] = (int)(sar[slot][j][par] >> (8 * g));
+    }
+#pragma unroll
+    for (int t = 0; t < NTB; t++) {
+      const v4i b0 = line_shuffle(br[slot][t][par][0], br[slot][t][par][1], 0, lo);
+      const v4i b1 = line_shuffle(br[slot][t][par][0], br[slot][t][par][1], 1, lo);
+      const v8i bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      const int sb = (int)(sbr[slot][t][par] >> (8 * g));
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const v8i aa = {a[j][0], a[j][1], a[j][2], a[j][3], 0, 0, 0, 0};
+        acc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, acc[j][t], 4, 0, 0, sa[j], 0, sb);
+      }
+    }
+  };
+
+  // Steady groups hold only full pairs and carry no branches; the waitcnt
+  // pass keeps the ring in flight across them (a guarded compute inside the
+  // loop made it drain every load before each pair).  The trailing pairs
+  // (at most PP, the last possibly a single stage) are already in flight.
+  const int last = npairs - 1;
+  const int full = nk / 2;  // pairs with both stages inside K
+#pragma unroll
+  for (int s = 0; s < PP; s++) load(s, s < npairs ? s : last);
+  int m0 = 0;
+  for (; m0 + PP <= full && m0 + PP < npairs; m0 += PP) {
+#pragma unroll
+    for (int s = 0; s < PP; s++) {
+      compute(s, 0);
+      compute(s, 1);
+      load(s, m0 + s + PP < npairs ? m0 + s + PP : last);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < PP; s++) {
+    const int m = m0 + s;
+    if (m < npairs) {
+      compute(s, 0);
+      if (2 * m + 1 < nk) compute(s, 1);
+    }
+  }
+
+  if (l1) {
+    const int i0 = blk * 32;
+#pragma unroll
+    for (int t = 0; t < NTB; t++) {
+      const int m = t * 16 + r16;
+      float hv[8];
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp);
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+      const int E = block_scale_exp(amax);
+      if (m < nrows) {
+        const size_t row = (size_t)(row0 + m);
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int j = 0; j < 4; j++) word |= f32_to_e4m3(__builtin_amdgcn_ldexpf(hv[hh * 4 + j], -E)) << (8 * j);
+          stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
+        }
+        if (g == 0) stg1(p.h_sf + row * (size_t)(I / 32) + (size_t)(i0 / 32), (uint8_t)(E + 127));
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < NTB; t++) {
+      const int m = t * 16 + r16;
+      if (m < nrows) {
+        const size_t row = (size_t)(row0 + m);
+#pragma unroll
+        for (int j = 0; j < 4; j++) stg16f(p.o + row * H + (size_t)(rb[j] + 4 * g), acc[j][t]);
+      }
+    }
+  }
+}
+
 
 // Tile queues.  Tile ids run over (expert, feature block, token block), token
 // block fastest, so tiles claimed together share a weight slice.
@@ -1025,7 +1231,12 @@ __device__ void phase_wave_tiles(const KParams& p, Shared& sh, const int* lr2s, 
     if (lane == 0) next = __hip_atomic_fetch_add(q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int e, mb, blk;
     decode_tile(sh, E, NB, (int)t, e, mb, blk);
-    wave_tile<RECIPE, BM>(p, sh, lr2s, local, l1, e, mb, blk);
+    if constexpr (RECIPE == 2) {
+      wave_tile_w4<BM>(p, sh, lr2s, local, l1, __builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(mb),
+                       __builtin_amdgcn_readfirstlane(blk));
+    } else {
+      wave_tile<RECIPE, BM>(p, sh, lr2s, local, l1, e, mb, blk);
+    }
   }
 }
 
