@@ -53,15 +53,25 @@ def algorithmic_bytes(p, active_experts: int) -> int:
 
 
 def traffic_from_profiles(workload: str):
-    """Measured HBM bytes per launch, when a counter summary for this exact kernel source exists."""
-    path = os.path.join(ROOT, "profiles", f"moe_ffn_kernel_{workload}_traffic.json")
+    """Measured HBM bytes per launch, when a counter summary for this exact kernel source exists.
+
+    The summary (profiles/moe_ffn_kernel_<workload>_traffic.md) holds the lines
+    `kernel_hash: <hash>` and `hbm_bytes_per_launch: <bytes>`."""
+    path = os.path.join(ROOT, "profiles", f"moe_ffn_kernel_{workload}_traffic.md")
     if not os.path.exists(path):
         return None
+    fields = {}
     with open(path) as fh:
-        d = json.load(fh)
-    if d.get("kernel_hash") != kernel_hash():
+        for line in fh:
+            if ":" in line and not line.startswith((" ", "|", "#")):
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_hash") != kernel_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def run_workload(name: str, steps: int, warmup: int, threads: int, log):
