@@ -1009,6 +1009,9 @@ __device__ void big_tile(const KParams& p, const Shared& sh, const BigRing& R, b
 // chunks 4-7; for the e4m3 rows: operand bytes 0-15 from chunks 0-3, bytes
 // 16-31 from chunks 4-7).
 // ---------------------------------------------------------------------------
+#ifndef MOEFFN_W4_PP
+#define MOEFFN_W4_PP 2
+#endif
 __device__ __forceinline__ int dpp_ror8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
 
 // lanes 0-7 of each 16-lane row take x0 (par 0) / rotated x0 (par 1); lanes 8-15 rotated x1 / x1
@@ -1026,7 +1029,7 @@ template <int BM>
 __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s, bool local, bool l1, int e, int mb,
                              int blk) {
   constexpr int NTB = BM / 16;
-  constexpr int PP = 2;  // weight pairs (2 K stages each) in flight
+  constexpr int PP = MOEFFN_W4_PP;  // weight pairs (2 K stages each) in flight
   const int lane = threadIdx.x & 63, g = lane >> 4, r16 = lane & 15;
   const bool lo = r16 < 8;
   const int H = p.H, I = p.I;
@@ -1088,19 +1091,25 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
   for (int j = 0; j < 4; j++)
 #pragma unroll
     for (int t = 0; t < NTB; t++) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  // Scales are fetched 16 bytes per row, for a group of two pairs (four K
+  // stages), with the refill of slot 0; slot 1 takes its pair's half of the
+  // group from a copy made before that refill.  Each scale load touches one
+  // cache line per row for only 8-16 useful bytes, so halving their number
+  // matters for the vector L1 (scale loads cost ~15% of the call at T=128).
+  static_assert(PP == 2, "scale groups pair slot 0 with slot 1");
   v4i ar[PP][4][2];          // weight pair: row block j, load half i
-  uint32_t sar[PP][4][2];    // weight scale dwords of the pair's two stages
   v4i br[PP][NTB][2][2];     // routed rows: block t, stage (0/1 of the pair), load half i
-  uint32_t sbr[PP][NTB][2];  // routed-row scale dwords
+  uint4 sga[4];              // weight scale dwords of the group: pair 0 stage 0/1, pair 1 stage 0/1
+  uint4 sgb[NTB];            // routed-row scale dwords of the group
+  uint2 nxa[4], nxb[NTB];    // the group's second pair, kept across the refill of slot 0
 
   auto load = [&](int slot, int m) {
 #pragma unroll
     for (int j = 0; j < 4; j++) {
 #pragma unroll
       for (int i = 0; i < 2; i++) ar[slot][j][i] = buf_load16(rW, a_voff, (uint32_t)(rb[j] + 8 * i) * arow + (uint32_t)m * 128);
-      const uint2 sv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rWs, as_voff, (uint32_t)rb[j] * srow + (uint32_t)m * 8, 0));
-      sar[slot][j][0] = sv.x;
-      sar[slot][j][1] = sv.y;
+      if (slot == 0)
+        sga[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rWs, as_voff, (uint32_t)rb[j] * srow + (uint32_t)m * 8, 0));
     }
 #pragma unroll
     for (int t = 0; t < NTB; t++) {
@@ -1108,31 +1117,39 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
       for (int st = 0; st < 2; st++)
 #pragma unroll
         for (int i = 0; i < 2; i++) br[slot][t][st][i] = buf_load16(rB, b_voff[t][i], (uint32_t)(2 * m + st) * 128);
-      const uint2 sv = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rBs, bs_voff[t], (uint32_t)m * 8, 0));
-      sbr[slot][t][0] = sv.x;
-      sbr[slot][t][1] = sv.y;
+      if (slot == 0)
+        sgb[t] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rBs, bs_voff[t], (uint32_t)m * 8, 0));
     }
   };
+  // scale dwords of the pair in `slot`: slot 0 reads the group directly, slot 1 the saved copy
   auto compute = [&](int slot, int par) {
     v4i a[4];
     int sa[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       a[j] = line_shuffle(ar[slot][j][0], ar[slot][j][1], par, lo);
-      sa[j] = (int)(sar[slot][j][par] >> (8 * g));
+      const uint32_t sw = slot == 0 ? (par == 0 ? sga[j].x : sga[j].y) : (par == 0 ? nxa[j].x : nxa[j].y);
+      sa[j] = (int)(sw >> (8 * g));
     }
 #pragma unroll
     for (int t = 0; t < NTB; t++) {
       const v4i b0 = line_shuffle(br[slot][t][par][0], br[slot][t][par][1], 0, lo);
       const v4i b1 = line_shuffle(br[slot][t][par][0], br[slot][t][par][1], 1, lo);
       const v8i bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
-      const int sb = (int)(sbr[slot][t][par] >> (8 * g));
+      const uint32_t sw = slot == 0 ? (par == 0 ? sgb[t].x : sgb[t].y) : (par == 0 ? nxb[t].x : nxb[t].y);
+      const int sb = (int)(sw >> (8 * g));
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const v8i aa = {a[j][0], a[j][1], a[j][2], a[j][3], 0, 0, 0, 0};
         acc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, acc[j][t], 4, 0, 0, sa[j], 0, sb);
       }
     }
+  };
+  auto save_group = [&]() {
+#pragma unroll
+    for (int j = 0; j < 4; j++) nxa[j] = uint2{sga[j].z, sga[j].w};
+#pragma unroll
+    for (int t = 0; t < NTB; t++) nxb[t] = uint2{sgb[t].z, sgb[t].w};
   };
 
   // Steady groups hold only full pairs and carry no branches; the waitcnt
@@ -1145,20 +1162,28 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
   for (int s = 0; s < PP; s++) load(s, s < npairs ? s : last);
   int m0 = 0;
   for (; m0 + PP <= full && m0 + PP < npairs; m0 += PP) {
-#pragma unroll
-    for (int s = 0; s < PP; s++) {
-      compute(s, 0);
-      compute(s, 1);
-      load(s, m0 + s + PP < npairs ? m0 + s + PP : last);
-    }
+    compute(0, 0);
+    compute(0, 1);
+    save_group();
+    // refill a slot only after its last use: interleaving the refill with the
+    // MFMAs lets register reuse force near-complete vmcnt drains
+    __builtin_amdgcn_sched_barrier(0);
+    load(0, m0 + PP);  // m0 + PP < npairs inside this loop
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, 0);
+    compute(1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load(1, m0 + 1 + PP < npairs ? m0 + 1 + PP : last);
+    __builtin_amdgcn_sched_barrier(0);
   }
-#pragma unroll
-  for (int s = 0; s < PP; s++) {
-    const int m = m0 + s;
-    if (m < npairs) {
-      compute(s, 0);
-      if (2 * m + 1 < nk) compute(s, 1);
-    }
+  save_group();
+  if (m0 < npairs) {
+    compute(0, 0);
+    if (2 * m0 + 1 < nk) compute(0, 1);
+  }
+  if (m0 + 1 < npairs) {
+    compute(1, 0);
+    if (2 * (m0 + 1) + 1 < nk) compute(1, 1);
   }
 
   if (l1) {
