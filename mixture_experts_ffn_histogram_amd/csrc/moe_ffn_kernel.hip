@@ -106,6 +106,8 @@ __device__ __forceinline__ void raise_status(const KParams& p, int code, bool fa
     st_relaxed(&p.ctrl->abort, 1u);
     st_relaxed(&p.ctrl->tile_next, kQueueClosed);   // every later claim lands past the last tile
     st_relaxed(&p.ctrl->tile_next2, kQueueClosed);
+    for (int l = 0; l < 2; l++)
+      for (int r = 0; r < 8; r++) st_relaxed(&p.ctrl->xq[l][r], kQueueClosed);
   }
 }
 
@@ -1288,25 +1290,67 @@ __device__ void phase_wg_tiles(const KParams& p, Shared& sh, SharedB<BM>& sb, co
   }
 }
 
-// 128-row tile phase (same queue order as the workgroup tiles).
+// 128-row tile phase.  The 8 XCDs of MI355X have separate L2 caches, so the
+// tile list is cut into 8 contiguous ranges, one per XCD, each with its own
+// claim counter: a workgroup drains the range of the XCD it runs on, then
+// takes tiles from the other ranges.  Inside an expert the tiles are ordered
+// in chunks of kBigGM token blocks x all feature blocks, token block fastest,
+// so the 32 workgroups of one XCD share about 32 / kBigGM weight slices and
+// kBigGM token blocks at a time and fetch each from outside the XCD once.
+constexpr int kBigGM = 4;
+
+__device__ __forceinline__ int xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return (int)(v & 7u);
+}
+
+// Tile t of the list -> expert e, token block mb, feature block nb.
+__device__ __forceinline__ void decode_big_tile(const Shared& sh, int E, int NB, int t, int& e, int& mb, int& nb) {
+  e = find_expert(sh.mbo, E, NB, t);
+  const int nmb_e = sh.mbo[e + 1] - sh.mbo[e];
+  const int loc = t - sh.mbo[e] * NB;
+  const int c = loc / (kBigGM * NB);
+  const int j = loc - c * kBigGM * NB;
+  const int gm = min(kBigGM, nmb_e - c * kBigGM);
+  nb = j / gm;
+  mb = c * kBigGM + (j - nb * gm);
+}
+
+// Claim the next tile (thread 0): own XCD's range first, then the others.
+// Returns n when every range is exhausted (or the queue is closed).
+__device__ __forceinline__ uint32_t claim_big_tile(uint32_t* ctr, uint32_t n, int home) {
+  for (int q = 0; q < 8; q++) {
+    const int r = (home + q) & 7;
+    const uint32_t beg = (uint32_t)(((uint64_t)n * (uint32_t)r) >> 3);
+    const uint32_t end = (uint32_t)(((uint64_t)n * (uint32_t)(r + 1)) >> 3);
+    if (end == beg) continue;
+    if (ld_relaxed(&ctr[r]) >= end - beg) continue;  // already drained: skip the atomic
+    const uint32_t c = __hip_atomic_fetch_add(&ctr[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c < end - beg) return beg + c;
+  }
+  return n;
+}
+
 template <int RECIPE>
 __device__ void phase_big_tiles(const KParams& p, Shared& sh, const BigRing& R, bool l1) {
   const int tid = threadIdx.x;
   const int E = p.E;
   const int NB = l1 ? p.I / 128 : (p.H + 255) / 256;
   const uint32_t n = (uint32_t)(sh.mbo[E] * NB);
-  uint32_t* q = l1 ? &p.ctrl->tile_next : &p.ctrl->tile_next2;
+  uint32_t* ctr = p.ctrl->xq[l1 ? 0 : 1];
+  const int home = xcc_id();
   uint32_t next = 0;
-  if (tid == 0) next = __hip_atomic_fetch_add(q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) next = claim_big_tile(ctr, n, home);
   for (;;) {
     if (tid == 0) sh.tile = next;
     __syncthreads();
     const uint32_t t = __builtin_amdgcn_readfirstlane(sh.tile);
     __syncthreads();
     if (t >= n) break;
-    if (tid == 0) next = __hip_atomic_fetch_add(q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) next = claim_big_tile(ctr, n, home);
     int e, mb, nb;
-    decode_tile(sh, E, NB, (int)t, e, mb, nb);
+    decode_big_tile(sh, E, NB, (int)t, e, mb, nb);
     big_tile<RECIPE>(p, sh, R, l1, __builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(mb),
                      __builtin_amdgcn_readfirstlane(nb));
   }
@@ -1428,6 +1472,8 @@ done:
       for (int i = 0; i < kNumBarriers; i++) st_relaxed(&p.ctrl->bar[i], 0u);
       st_relaxed(&p.ctrl->tile_next, 0u);
       st_relaxed(&p.ctrl->tile_next2, 0u);
+      for (int l = 0; l < 2; l++)
+        for (int r = 0; r < 8; r++) st_relaxed(&p.ctrl->xq[l][r], 0u);
       st_relaxed(&p.ctrl->abort, 0u);
       __hip_atomic_store(&p.ctrl->status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       st_release(&p.ctrl->exit_count, 0u);

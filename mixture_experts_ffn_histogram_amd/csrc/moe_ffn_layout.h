@@ -28,12 +28,14 @@ struct Ctrl {
   uint32_t tile_next2;         // next L2 tile to claim
   uint32_t abort;              // set on a fatal condition: every wait gives up
   int32_t status;              // first MOE_FFN_STATUS_* of the call
-  uint32_t pad[53];
+  uint32_t xq[2][8];           // 128-row tiles: per-XCD range claim counters (L1, L2)
+  uint32_t pad[37];
 };
 static_assert(sizeof(Ctrl) == 256, "control block must stay 256 bytes");
 static_assert(offsetof(Ctrl, bar) == 0, "barrier counters lead the control block");
 static_assert(offsetof(Ctrl, exit_count) == 24, "layout change must be deliberate");
 static_assert(offsetof(Ctrl, status) == 40, "layout change must be deliberate");
+static_assert(offsetof(Ctrl, xq) == 44, "layout change must be deliberate");
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
