@@ -44,5 +44,21 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     return LIB
 
 
+def build_test_helpers(verbose: bool = False) -> str:
+    """Compile the test-only side-stream helper (tests/native) for gfx950."""
+    root = os.path.dirname(HERE)
+    src = os.path.join(root, "tests", "native", "side_kernel.hip")
+    out = os.path.join(root, "tests", "native", "libmoe_side.so")
+    cmd = [HIPCC] + COMMON + ["-shared", "-x", "hip", src, "-o", out + ".tmp"]
+    if verbose:
+        print(" ".join(cmd))
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed on the side-stream test helper")
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True, resource_usage="--usage" in sys.argv))

@@ -183,3 +183,14 @@ def assert_h_decisions(run: "Runner", p: dict, rows, clamp: float):
         assert not bad.any(), f"row {r}: {int(bad.sum())} codes outside the band (first at {np.where(bad)[0][:5]})"
         flips += int((diff > 0).sum())
     return flips
+
+
+def check_tables(run: "Runner", p: dict, T: int) -> None:
+    """Routing outputs of the last call equal the oracle's bit for bit."""
+    idx = p["topk_idx"][:T]
+    counts, offsets, r2s, s2r, _ = oracle.route(idx, p["E"])
+    g_counts, g_off, g_r2s, g_s2r = run.tables(T)
+    assert np.array_equal(g_counts, counts)
+    assert np.array_equal(g_off, offsets)
+    assert np.array_equal(g_r2s, r2s)
+    assert np.array_equal(g_s2r, s2r)

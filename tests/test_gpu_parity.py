@@ -11,20 +11,14 @@ import torch
 
 import oracle
 from mixture_experts_ffn_histogram_amd import synth
-from gpu_common import (Runner, assert_h_decisions, assert_y_parity, log, oracle_y, oracle_y_band,
+from gpu_common import (Runner, assert_h_decisions, assert_y_parity, check_tables, log, oracle_y, oracle_y_band,
                         rel_err, tol_for, upload_inputs)
 
 pytestmark = pytest.mark.gpu
 
 
 def _check_tables(run: Runner, p: dict, T: int):
-    idx = p["topk_idx"][:T]
-    counts, offsets, r2s, s2r, _ = oracle.route(idx, p["E"])
-    g_counts, g_off, g_r2s, g_s2r = run.tables(T)
-    assert np.array_equal(g_counts, counts)
-    assert np.array_equal(g_off, offsets)
-    assert np.array_equal(g_r2s, r2s)
-    assert np.array_equal(g_s2r, s2r)
+    check_tables(run, p, T)
 
 
 def _small_cfg(recipe, T, H, I, E, k, routing="softmax", seed=7, y_fp32=False):
