@@ -790,8 +790,15 @@ constexpr int kBigBM = 128, kBigNB = 3, kBigD = 2, kBigP = 3;
 constexpr int kBigBsf = kBigBM * 128;               // routed-row scale dwords (+ a second copy)
 constexpr int kBigAsf = kBigBsf + 2 * kBigBM * 4;   // weight-row scale dwords
 constexpr int kBigBuf = kBigAsf + 256 * 4;          // 18432 bytes per stage
-constexpr int kBigWait = 4 + 10 * (kBigD - 1);      // younger VMEM ops allowed when stage s is consumed
 static_assert(kBigP == kBigNB && kBigD == kBigNB - 1, "ring indices assume P = NB = D + 1");
+// Younger VMEM operations allowed when stage s is consumed: the weight loads
+// of iteration s-D (4) and all of iteration s-1 (row pieces, 2 scale fills,
+// 4 weight loads).  A tile of NT 16-row blocks fills NT/2 (at least 1) row
+// pieces per wave and stage.
+template <int NT>
+constexpr int big_row_pieces() { return NT >= 2 ? NT / 2 : 1; }
+template <int NT>
+constexpr int big_wait() { return 4 + (big_row_pieces<NT>() + 6) * (kBigD - 1); }
 
 struct BigRing {
   uint8_t* b0;
@@ -799,49 +806,57 @@ struct BigRing {
   uint8_t* b2;
 };
 
-__device__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __restrict__ B1, uint8_t* __restrict__ B2,
-                          v4f (&acc)[4][8], rsrc_t rW, uint32_t a_off, const uint32_t (&a_soff)[4], rsrc_t rWs,
-                          uint32_t as_off, rsrc_t rX, uint32_t xa_off, uint32_t xb_off, rsrc_t rXs,
-                          uint32_t xs_off, int nk, int wave, int lane) {
+template <int NT>
+__device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __restrict__ B1, uint8_t* __restrict__ B2,
+                                          v4f (&acc)[4][NT], rsrc_t rW, uint32_t a_off, const uint32_t (&a_soff)[4],
+                                          rsrc_t rWs, uint32_t as_off, rsrc_t rX, uint32_t xa_off, uint32_t xb_off,
+                                          rsrc_t rXs, uint32_t xs_off, int nk, int wave, int lane) {
+  constexpr int RP = big_row_pieces<NT>();
   const int g = lane >> 4, r16 = lane & 15;
   auto BUF = [&](int u) -> uint8_t* { return u == 0 ? B0 : u == 1 ? B1 : B2; };
 #pragma unroll
   for (int j = 0; j < 4; j++)
 #pragma unroll
-    for (int t = 0; t < 8; t++) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < NT; t++) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
   v4i ar[kBigP][4];
 
   auto load_a = [&](int slot, int s) {
 #pragma unroll
     for (int j = 0; j < 4; j++) ar[slot][j] = buf_load16(rW, a_off, a_soff[j] + (uint32_t)s * 64);
   };
-  // Stage s into ring buffer `buf`: 16 x 1 KB of routed-row bytes (piece
+  // Stage s into ring buffer `buf`: 2*NT x 1 KB of routed-row bytes (piece
   // (t, half) holds bytes half*64 + g*16 .. +16 of row t*16 + c at lane
-  // g*16 + c: the e4m3 MFMA operand layout), the routed-row scale dwords
-  // (waves 2-3 write a second copy so every wave issues the same count) and
-  // the weight-row scale dwords of the wave's 64 rows.
+  // g*16 + c: the e4m3 MFMA operand layout; wave w fills pieces
+  // RP*w .. RP*w + RP-1, at NT = 2 only waves 0-3 of the 4 pieces), the
+  // routed-row scale dwords (waves that map to the same rows write extra
+  // copies so every wave issues the same count) and the weight-row scale
+  // dwords of the wave's 64 rows.
   auto dma = [&](int s, int buf) {
     uint8_t* bp = BUF(buf);
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      buf_load_lds16(rX, bp + (wave * 4 + i) * 1024, (i >> 1) ? xb_off : xa_off, (uint32_t)s * 128 + (i & 1) * 64);
-    buf_load_lds4(rXs, bp + kBigBsf + ((wave >> 1) * kBigBM + (wave & 1) * 64) * 4, xs_off, (uint32_t)s * 4);
+    for (int i = 0; i < RP; i++) {
+      const int piece = wave * RP + i;
+      buf_load_lds16(rX, bp + piece * 1024, (NT == 8 && i >= 2) ? xb_off : xa_off,
+                     (uint32_t)s * 128 + (uint32_t)(piece & 1) * 64);
+    }
+    const int scopy = NT == 8 ? ((wave >> 1) * kBigBM + (wave & 1) * 64) : wave * 64;
+    buf_load_lds4(rXs, bp + kBigBsf + scopy * 4, xs_off, (uint32_t)s * 4);
     buf_load_lds4(rWs, bp + kBigAsf + wave * 64 * 4, as_off, (uint32_t)s * 4);
   };
   auto compute = [&](int slot, int buf) {
     const uint8_t* bp = BUF(buf);
-    int sa[4], sb[8];
+    int sa[4], sb[NT];
 #pragma unroll
     for (int j = 0; j < 4; j++) sa[j] = bp[kBigAsf + (wave * 64 + j * 16 + r16) * 4 + g];
 #pragma unroll
-    for (int t = 0; t < 8; t++) sb[t] = bp[kBigBsf + (t * 16 + r16) * 4 + g];
+    for (int t = 0; t < NT; t++) sb[t] = bp[kBigBsf + (t * 16 + r16) * 4 + g];
     v4i n0 = *(const v4i*)(bp + (0 * 64 + lane) * 16);
     v4i n1 = *(const v4i*)(bp + (1 * 64 + lane) * 16);
-    __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 6 + NT, 0);
 #pragma unroll
-    for (int t = 0; t < 8; t++) {
+    for (int t = 0; t < NT; t++) {
       const v8i bb = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3]};
-      if (t < 7) {
+      if (t < NT - 1) {
         n0 = *(const v4i*)(bp + (((t + 1) * 2) * 64 + lane) * 16);
         n1 = *(const v4i*)(bp + (((t + 1) * 2 + 1) * 64 + lane) * 16);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -874,7 +889,7 @@ __device__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __restrict__ B1, ui
 #pragma unroll
     for (int u = 0; u < kBigP; u++) {
       const int s = s0 + u;
-      MOEFFN_WAIT_VMCNT(kBigWait);        // this wave's fill of stage s has landed
+      MOEFFN_WAIT_VMCNT(big_wait<NT>());  // this wave's fill of stage s has landed
       __builtin_amdgcn_s_barrier();       // ... and every other wave's
       dma(s + kBigD < nk ? s + kBigD : nk - 1, (u + kBigD) % kBigNB);
       __builtin_amdgcn_sched_barrier(0);
@@ -900,8 +915,11 @@ __device__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __restrict__ B1, ui
 // One 128-row tile: expert e, token block mb, feature block nb (L1: 128
 // intermediate features = 4 waves x (32 gate + 32 up rows); L2: 256 hidden
 // outputs = 4 waves x 64 rows).
-template <int RECIPE>
-__device__ void big_tile(const KParams& p, const Shared& sh, const BigRing& R, bool l1, int e, int mb, int nb) {
+// NT: 16-row blocks computed (the tile's rows rounded up to 16, as 2, 4 or
+// 8): a partly filled last token block of an expert skips the MFMAs and the
+// routed-row fills of its empty blocks.
+template <int RECIPE, int NT>
+__device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, const BigRing& R, bool l1, int e, int mb, int nb) {
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, r16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
   const int H = p.H, I = p.I;
@@ -930,9 +948,11 @@ __device__ void big_tile(const KParams& p, const Shared& sh, const BigRing& R, b
   const uint32_t a_off = (uint32_t)r16 * arow + (uint32_t)g * 16;
   const uint32_t as_off = (uint32_t)(rb[lane >> 4] + r16) * srow;
 
-  // routed rows of the tile (rows past the expert repeat its first row / read padding)
+  // routed rows of the tile (rows past the expert repeat its first row / read padding):
+  // the row pieces of this wave cover 16-row blocks ta (and tb at NT = 8)
   const int c = r16;
-  const int ma = (wave * 2) * 16 + c, mbb = (wave * 2 + 1) * 16 + c, ms = (wave & 1) * 64 + lane;
+  const int ta = NT == 8 ? wave * 2 : NT == 4 ? wave : wave >> 1;
+  const int ma = ta * 16 + c, mbb = (ta + 1) * 16 + c, ms = NT == 8 ? (wave & 1) * 64 + lane : lane;
   rsrc_t rX, rXs;
   uint32_t xa_off, xb_off, xs_off;
   if (l1) {
@@ -953,14 +973,14 @@ __device__ void big_tile(const KParams& p, const Shared& sh, const BigRing& R, b
     xs_off = (uint32_t)(row0 + ms) * (uint32_t)(I / 32);
   }
 
-  v4f acc[4][8];
-  big_kloop(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, rX, xa_off, xb_off, rXs, xs_off, nk, wave, lane);
+  v4f acc[4][NT];
+  big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, rX, xa_off, xb_off, rXs, xs_off, nk, wave, lane);
 
   if (!active) return;
   if (l1) {
     const int i0 = rb[0];
 #pragma unroll
-    for (int t = 0; t < 8; t++) {
+    for (int t = 0; t < NT; t++) {
       const int m = t * 16 + r16;
       float hv[8];
 #pragma unroll
@@ -987,7 +1007,7 @@ __device__ void big_tile(const KParams& p, const Shared& sh, const BigRing& R, b
     }
   } else {
 #pragma unroll
-    for (int t = 0; t < 8; t++) {
+    for (int t = 0; t < NT; t++) {
       const int m = t * 16 + r16;
       if (m < nrows) {
         const size_t row = (size_t)(row0 + m);
@@ -1333,7 +1353,7 @@ __device__ __forceinline__ uint32_t claim_big_tile(uint32_t* ctr, uint32_t n, in
 }
 
 template <int RECIPE>
-__device__ void phase_big_tiles(const KParams& p, Shared& sh, const BigRing& R, bool l1) {
+__device__ __forceinline__ void phase_big_tiles(const KParams& p, Shared& sh, const BigRing& R, bool l1) {
   const int tid = threadIdx.x;
   const int E = p.E;
   const int NB = l1 ? p.I / 128 : (p.H + 255) / 256;
@@ -1351,8 +1371,13 @@ __device__ void phase_big_tiles(const KParams& p, Shared& sh, const BigRing& R, 
     if (tid == 0) next = claim_big_tile(ctr, n, home);
     int e, mb, nb;
     decode_big_tile(sh, E, NB, (int)t, e, mb, nb);
-    big_tile<RECIPE>(p, sh, R, l1, __builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(mb),
-                     __builtin_amdgcn_readfirstlane(nb));
+    e = __builtin_amdgcn_readfirstlane(e);
+    mb = __builtin_amdgcn_readfirstlane(mb);
+    nb = __builtin_amdgcn_readfirstlane(nb);
+    const int nrows = __builtin_amdgcn_readfirstlane(min(kBigBM, sh.cnt[e] - mb * kBigBM));
+    if (nrows > 64) big_tile<RECIPE, 8>(p, sh, R, l1, e, mb, nb);
+    else if (nrows > 32) big_tile<RECIPE, 4>(p, sh, R, l1, e, mb, nb);
+    else big_tile<RECIPE, 2>(p, sh, R, l1, e, mb, nb);
   }
 }
 
