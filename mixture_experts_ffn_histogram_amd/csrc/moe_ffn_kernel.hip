@@ -828,9 +828,9 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
   // (t, half) holds bytes half*64 + g*16 .. +16 of row t*16 + c at lane
   // g*16 + c: the e4m3 MFMA operand layout; wave w fills pieces
   // RP*w .. RP*w + RP-1, at NT = 2 only waves 0-3 of the 4 pieces), the
-  // routed-row scale dwords (waves that map to the same rows write extra
-  // copies so every wave issues the same count) and the weight-row scale
-  // dwords of the wave's 64 rows.
+  // routed-row scale dwords (waves beyond the first copy load zeros from
+  // past the end of the buffer into further copies, so every wave issues
+  // the same count) and the weight-row scale dwords of the wave's 64 rows.
   auto dma = [&](int s, int buf) {
     uint8_t* bp = BUF(buf);
 #pragma unroll
@@ -972,6 +972,11 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
     xb_off = (uint32_t)(row0 + mbb) * (uint32_t)I + (uint32_t)g * 16;
     xs_off = (uint32_t)(row0 + ms) * (uint32_t)(I / 32);
   }
+  // A wave whose scale dwords would repeat rows another wave already loads
+  // reads past the end of the buffer instead: that load returns zeros without
+  // a memory access (each dword it would fetch is a cache line of its own),
+  // and every wave still issues the same count.
+  if (NT == 8 ? wave >= 2 : wave >= 1) xs_off = 0x80000000u;
 
   v4f acc[4][NT];
   big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, rX, xa_off, xb_off, rXs, xs_off, nk, wave, lane);
