@@ -809,8 +809,9 @@ struct BigRing {
 template <int NT>
 __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __restrict__ B1, uint8_t* __restrict__ B2,
                                           v4f (&acc)[4][NT], rsrc_t rW, uint32_t a_off, const uint32_t (&a_soff)[4],
-                                          rsrc_t rWs, uint32_t as_off, rsrc_t rX, uint32_t xa_off, uint32_t xb_off,
-                                          rsrc_t rXs, uint32_t xs_off, int nk, int wave, int lane) {
+                                          rsrc_t rWs, uint32_t as_off, rsrc_t rX, const uint32_t (&xoff)[4],
+                                          uint32_t brd0, uint32_t brd1, rsrc_t rXs, uint32_t xs_off, int nk, int wave,
+                                          int lane) {
   constexpr int RP = big_row_pieces<NT>();
   const int g = lane >> 4, r16 = lane & 15;
   auto BUF = [&](int u) -> uint8_t* { return u == 0 ? B0 : u == 1 ? B1 : B2; };
@@ -824,21 +825,18 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
 #pragma unroll
     for (int j = 0; j < 4; j++) ar[slot][j] = buf_load16(rW, a_off, a_soff[j] + (uint32_t)s * 64);
   };
-  // Stage s into ring buffer `buf`: 2*NT x 1 KB of routed-row bytes (piece
-  // (t, half) holds bytes half*64 + g*16 .. +16 of row t*16 + c at lane
-  // g*16 + c: the e4m3 MFMA operand layout; wave w fills pieces
-  // RP*w .. RP*w + RP-1, at NT = 2 only waves 0-3 of the 4 pieces), the
-  // routed-row scale dwords (waves beyond the first copy load zeros from
-  // past the end of the buffer into further copies, so every wave issues
-  // the same count) and the weight-row scale dwords of the wave's 64 rows.
+  // Stage s into ring buffer `buf`: 2*NT x 1 KB of routed-row bytes, whole
+  // 128-byte lines: instruction q holds rows 8q..8q+7, its lane l row
+  // 8q + (l%16)/2, 16-byte chunk 4*((l&1)^(q&1)) + l/16 (wave w issues
+  // q = RP*w .. RP*w + RP-1; brd0/brd1 address a lane's MFMA operand bytes
+  // 0-15 / 16-31 of routed-row block 0), the routed-row scale dwords (waves
+  // beyond the first copy load zeros from past the end of the buffer into
+  // further copies, so every wave issues the same count) and the weight-row
+  // scale dwords of the wave's 64 rows.
   auto dma = [&](int s, int buf) {
     uint8_t* bp = BUF(buf);
 #pragma unroll
-    for (int i = 0; i < RP; i++) {
-      const int piece = wave * RP + i;
-      buf_load_lds16(rX, bp + piece * 1024, (NT == 8 && i >= 2) ? xb_off : xa_off,
-                     (uint32_t)s * 128 + (uint32_t)(piece & 1) * 64);
-    }
+    for (int i = 0; i < RP; i++) buf_load_lds16(rX, bp + (wave * RP + i) * 1024, xoff[i], (uint32_t)s * 128);
     const int scopy = NT == 8 ? ((wave >> 1) * kBigBM + (wave & 1) * 64) : wave * 64;
     buf_load_lds4(rXs, bp + kBigBsf + scopy * 4, xs_off, (uint32_t)s * 4);
     buf_load_lds4(rWs, bp + kBigAsf + wave * 64 * 4, as_off, (uint32_t)s * 4);
@@ -850,15 +848,15 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
     for (int j = 0; j < 4; j++) sa[j] = bp[kBigAsf + (wave * 64 + j * 16 + r16) * 4 + g];
 #pragma unroll
     for (int t = 0; t < NT; t++) sb[t] = bp[kBigBsf + (t * 16 + r16) * 4 + g];
-    v4i n0 = *(const v4i*)(bp + (0 * 64 + lane) * 16);
-    v4i n1 = *(const v4i*)(bp + (1 * 64 + lane) * 16);
+    v4i n0 = *(const v4i*)(bp + brd0);
+    v4i n1 = *(const v4i*)(bp + brd1);
     __builtin_amdgcn_sched_group_barrier(0x100, 6 + NT, 0);
 #pragma unroll
     for (int t = 0; t < NT; t++) {
       const v8i bb = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3]};
       if (t < NT - 1) {
-        n0 = *(const v4i*)(bp + (((t + 1) * 2) * 64 + lane) * 16);
-        n1 = *(const v4i*)(bp + (((t + 1) * 2 + 1) * 64 + lane) * 16);
+        n0 = *(const v4i*)(bp + brd0 + (t + 1) * 2048);
+        n1 = *(const v4i*)(bp + brd1 + (t + 1) * 2048);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
 #pragma unroll
@@ -948,30 +946,36 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   const uint32_t a_off = (uint32_t)r16 * arow + (uint32_t)g * 16;
   const uint32_t as_off = (uint32_t)(rb[lane >> 4] + r16) * srow;
 
-  // routed rows of the tile (rows past the expert repeat its first row / read padding):
-  // the row pieces of this wave cover 16-row blocks ta (and tb at NT = 8)
-  const int c = r16;
-  const int ta = NT == 8 ? wave * 2 : NT == 4 ? wave : wave >> 1;
-  const int ma = ta * 16 + c, mbb = (ta + 1) * 16 + c, ms = NT == 8 ? (wave & 1) * 64 + lane : lane;
+  // routed rows of the tile (rows past the expert repeat its first row / read
+  // padding): fill instruction i of this wave covers rows 8*(RP*wave + i) + (l%16)/2
+  constexpr int RP = big_row_pieces<NT>();
+  const int c8 = r16 >> 1;
+  const int ms = NT == 8 ? (wave & 1) * 64 + lane : lane;
   rsrc_t rX, rXs;
-  uint32_t xa_off, xb_off, xs_off;
+  uint32_t xoff[4] = {0u, 0u, 0u, 0u}, xs_off;
   if (l1) {
-    const uint32_t ta = (uint32_t)(route_slot(p, nullptr, false, row0 + (ma < nrows ? ma : 0)) / p.k);
-    const uint32_t tb = (uint32_t)(route_slot(p, nullptr, false, row0 + (mbb < nrows ? mbb : 0)) / p.k);
-    const uint32_t ts = (uint32_t)(route_slot(p, nullptr, false, row0 + (ms < nrows ? ms : 0)) / p.k);
     rX = make_rsrc(p.x, (uint32_t)p.T * (uint32_t)H);
     rXs = make_rsrc(p.x_sf, (uint32_t)p.T * (uint32_t)(H / 32));
-    xa_off = ta * (uint32_t)H + (uint32_t)g * 16;
-    xb_off = tb * (uint32_t)H + (uint32_t)g * 16;
-    xs_off = ts * (uint32_t)(H / 32);
+#pragma unroll
+    for (int i = 0; i < RP; i++) {
+      const int q = wave * RP + i, m = 8 * q + c8;
+      const uint32_t tok = (uint32_t)(route_slot(p, nullptr, false, row0 + (m < nrows ? m : 0)) / p.k);
+      xoff[i] = tok * (uint32_t)H + (uint32_t)((((lane & 1) ^ (q & 1)) * 4 + g) * 16);
+    }
+    xs_off = (uint32_t)(route_slot(p, nullptr, false, row0 + (ms < nrows ? ms : 0)) / p.k) * (uint32_t)(H / 32);
   } else {
     const uint32_t rows_end = (uint32_t)(row0 + kBigBM);  // h is padded by kMaxBM rows
     rX = make_rsrc(p.h, rows_end * (uint32_t)I);
     rXs = make_rsrc(p.h_sf, rows_end * (uint32_t)(I / 32));
-    xa_off = (uint32_t)(row0 + ma) * (uint32_t)I + (uint32_t)g * 16;
-    xb_off = (uint32_t)(row0 + mbb) * (uint32_t)I + (uint32_t)g * 16;
+#pragma unroll
+    for (int i = 0; i < RP; i++) {
+      const int q = wave * RP + i;
+      xoff[i] = (uint32_t)(row0 + 8 * q + c8) * (uint32_t)I + (uint32_t)((((lane & 1) ^ (q & 1)) * 4 + g) * 16);
+    }
     xs_off = (uint32_t)(row0 + ms) * (uint32_t)(I / 32);
   }
+  const uint32_t brd0 = (uint32_t)(((r16 >> 3) * 64 + g * 16 + 2 * (r16 & 7) + (0 ^ (r16 >> 3))) * 16);
+  const uint32_t brd1 = (uint32_t)(((r16 >> 3) * 64 + g * 16 + 2 * (r16 & 7) + (1 ^ (r16 >> 3))) * 16);
   // A wave whose scale dwords would repeat rows another wave already loads
   // reads past the end of the buffer instead: that load returns zeros without
   // a memory access (each dword it would fetch is a cache line of its own),
@@ -979,7 +983,8 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   if (NT == 8 ? wave >= 2 : wave >= 1) xs_off = 0x80000000u;
 
   v4f acc[4][NT];
-  big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, rX, xa_off, xb_off, rXs, xs_off, nk, wave, lane);
+  big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, rX, xoff, brd0, brd1, rXs, xs_off, nk, wave,
+                lane);
 
   if (!active) return;
   if (l1) {
