@@ -98,6 +98,13 @@ typedef struct {
     int32_t* row_to_slot;        /* optional [T*k] device out: first R = offsets[E] entries written  */
     int32_t* slot_to_row;        /* optional [T*k] device out: row of each slot, -1 when masked      */
     int32_t* status;             /* optional device int: MOE_FFN_STATUS_* of this call               */
+    const uint8_t* w1_sf_kmajor; /* optional, e2m1 recipe: w1_sf in K-major order [E, H/32, 2I], as   */
+                                 /* written by moe_ffn_transform_weight_scales; NULL = not given      */
+    const uint8_t* w2_sf_kmajor; /* optional, e2m1 recipe: w2_sf as [E, I/32, H]; NULL = not given   */
+                                 /* The 128-row tiles of large calls need both K-major copies (their */
+                                 /* per-stage scale fills then read contiguous rows); without them a */
+                                 /* large e2m1 call runs on 64-row tiles.  Both must hold the same   */
+                                 /* values as w1_sf / w2_sf.                                          */
 } moe_ffn_args;
 
 /* Bytes of device workspace one in-flight call needs (buffer-size query of the
@@ -117,6 +124,19 @@ int moe_ffn_get_token_alignment(int32_t recipe, int64_t* alignment);
    global state). */
 int moe_ffn_forward(const moe_ffn_problem* problem, const moe_ffn_args* args,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Weight-scale transform (the weight transform step of the pages' host API,
+   done once per set of weights): dst[e][b][r] = src[e][r][b] for e <
+   num_experts, r < rows, b < k_blocks, i.e. the e8m0 scales of each expert's
+   weight matrix re-ordered K-major.  For W1 rows = 2I, k_blocks = H/32; for
+   W2 rows = H, k_blocks = I/32.  src and dst are device buffers of
+   num_experts*rows*k_blocks bytes that must not overlap; dst must be 4-byte
+   aligned.  Enqueued on `stream` (a hipStream_t; NULL = default stream);
+   asynchronous, allocates nothing.  Returns MOE_FFN_ERR_INVALID_ARG for null
+   pointers, non-positive sizes, rows not a multiple of 4 or a misaligned
+   dst, MOE_FFN_ERR_HIP when the launch fails. */
+int moe_ffn_transform_weight_scales(const uint8_t* src, uint8_t* dst, int64_t num_experts, int64_t rows,
+                                    int64_t k_blocks, void* stream);
 
 /* Text of a return or status code (static string). */
 const char* moe_ffn_strerror(int code);

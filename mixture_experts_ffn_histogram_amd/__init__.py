@@ -47,7 +47,8 @@ class Args(ctypes.Structure):
                 ("reserved_cus", ctypes.c_int32), ("max_cus", ctypes.c_int32),
                 ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
                 ("row_to_slot", ctypes.c_void_p), ("slot_to_row", ctypes.c_void_p),
-                ("status", ctypes.c_void_p)]
+                ("status", ctypes.c_void_p),
+                ("w1_sf_kmajor", ctypes.c_void_p), ("w2_sf_kmajor", ctypes.c_void_p)]
 
 
 class WorkspaceView(ctypes.Structure):
@@ -57,7 +58,8 @@ class WorkspaceView(ctypes.Structure):
 
 
 EXPORTS = ("moe_ffn_get_workspace_size", "moe_ffn_get_token_alignment", "moe_ffn_forward",
-           "moe_ffn_strerror", "moe_ffn_launch_size", "moe_ffn_get_workspace_view")
+           "moe_ffn_strerror", "moe_ffn_launch_size", "moe_ffn_get_workspace_view",
+           "moe_ffn_transform_weight_scales")
 
 _lib = None
 
@@ -83,6 +85,8 @@ def lib():
         L.moe_ffn_launch_size.restype = ctypes.c_int
         L.moe_ffn_get_workspace_view.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(WorkspaceView)]
         L.moe_ffn_get_workspace_view.restype = ctypes.c_int
+        L.moe_ffn_transform_weight_scales.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
+        L.moe_ffn_transform_weight_scales.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -134,10 +138,31 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def transform_weight_scales(src, dst, num_experts: int, rows: int, k_blocks: int, stream=None) -> None:
+    """Enqueue moe_ffn_transform_weight_scales: dst[e][b][r] = src[e][r][b] (uint8 device tensors)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rc = lib().moe_ffn_transform_weight_scales(_ptr(src), _ptr(dst), int(num_experts), int(rows), int(k_blocks),
+                                               ctypes.c_void_p(stream.cuda_stream))
+    _check(rc, "moe_ffn_transform_weight_scales")
+
+
+def kmajor_weight_scales(w1_sf, w2_sf, num_experts: int, hidden: int, intermediate: int, stream=None):
+    """K-major copies of W1's and W2's scales (new device tensors), for the 128-row tiles."""
+    import torch
+    a = torch.empty_like(w1_sf)
+    b = torch.empty_like(w2_sf)
+    transform_weight_scales(w1_sf, a, num_experts, 2 * intermediate, hidden // 32, stream)
+    transform_weight_scales(w2_sf, b, num_experts, hidden, intermediate // 32, stream)
+    return a, b
+
+
 def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, topk_weights,
             w1, w1_sf, w2, w2_sf, y, y_dtype: int, activation_clamp: float,
             reserved_cus: int = -1, max_cus: int = 0, expert_counts=None, expert_offsets=None,
-            row_to_slot=None, slot_to_row=None, status=None, stream=None) -> None:
+            row_to_slot=None, slot_to_row=None, status=None, stream=None, w1_sf_kmajor=None,
+            w2_sf_kmajor=None) -> None:
     """Enqueue moe_ffn_forward on `stream` (default: torch's current stream).
 
     All tensors are device tensors laid out as include/moe_ffn.h states; the
@@ -150,7 +175,7 @@ def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, 
     a = Args(int(num_tokens), _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),
              _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf), _ptr(y), int(y_dtype), float(activation_clamp),
              int(reserved_cus), int(max_cus), _ptr(expert_counts), _ptr(expert_offsets),
-             _ptr(row_to_slot), _ptr(slot_to_row), _ptr(status))
+             _ptr(row_to_slot), _ptr(slot_to_row), _ptr(status), _ptr(w1_sf_kmajor), _ptr(w2_sf_kmajor))
     rc = lib().moe_ffn_forward(ctypes.byref(problem), ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                ctypes.c_void_p(stream.cuda_stream))

@@ -25,6 +25,8 @@ struct KParams {
   const uint8_t* w1_sf;
   const uint8_t* w2;
   const uint8_t* w2_sf;
+  const uint8_t* w1_sf_km;  // K-major copies of the weight scales (128-row tiles)
+  const uint8_t* w2_sf_km;
   void* y;
   // optional outputs
   int32_t* out_counts;
@@ -47,6 +49,10 @@ struct KParams {
 // Launches the persistent kernel for `recipe` with token block `bm` on `grid`
 // workgroups.  Returns the hipError_t of the launch.
 hipError_t launch_forward(int recipe, int bm, int grid, const KParams& p, hipStream_t stream);
+
+// dst[e][b][r] = src[e][r][b] (e < E, r < rows, b < kb): weight scales re-ordered K-major.
+hipError_t launch_transform_scales(const uint8_t* src, uint8_t* dst, int64_t E, int64_t rows, int64_t kb,
+                                   hipStream_t stream);
 
 // Largest token block the recipe supports (register budget of the A ring).
 int max_block_m(int recipe);

@@ -809,7 +809,8 @@ struct BigRing {
 template <int NT>
 __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __restrict__ B1, uint8_t* __restrict__ B2,
                                           v4f (&acc)[4][NT], rsrc_t rW, uint32_t a_off, const uint32_t (&a_soff)[4],
-                                          rsrc_t rWs, uint32_t as_off, rsrc_t rX, const uint32_t (&xoff)[4],
+                                          rsrc_t rWs, uint32_t as_off, uint32_t ws_stride, uint32_t sa_base,
+                                          const int (&sa_j)[4], rsrc_t rX, const uint32_t (&xoff)[4],
                                           uint32_t brd0, uint32_t brd1, rsrc_t rXs, uint32_t xs_off, int nk, int wave,
                                           int lane) {
   constexpr int RP = big_row_pieces<NT>();
@@ -832,20 +833,22 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
   // 0-15 / 16-31 of routed-row block 0), the routed-row scale dwords (waves
   // beyond the first copy load zeros from past the end of the buffer into
   // further copies, so every wave issues the same count) and the weight-row
-  // scale dwords of the wave's 64 rows.
+  // scales of the stage from the K-major copy: wave w fetches block 4s+w of
+  // the tile's 256 weight rows (contiguous runs of 128 or 256 bytes), stored
+  // as [block][tile row].
   auto dma = [&](int s, int buf) {
     uint8_t* bp = BUF(buf);
 #pragma unroll
     for (int i = 0; i < RP; i++) buf_load_lds16(rX, bp + (wave * RP + i) * 1024, xoff[i], (uint32_t)s * 128);
     const int scopy = NT == 8 ? ((wave >> 1) * kBigBM + (wave & 1) * 64) : wave * 64;
     buf_load_lds4(rXs, bp + kBigBsf + scopy * 4, xs_off, (uint32_t)s * 4);
-    buf_load_lds4(rWs, bp + kBigAsf + wave * 64 * 4, as_off, (uint32_t)s * 4);
+    buf_load_lds4(rWs, bp + kBigAsf + wave * 256, as_off, (uint32_t)(4 * s + wave) * ws_stride);
   };
   auto compute = [&](int slot, int buf) {
     const uint8_t* bp = BUF(buf);
     int sa[4], sb[NT];
 #pragma unroll
-    for (int j = 0; j < 4; j++) sa[j] = bp[kBigAsf + (wave * 64 + j * 16 + r16) * 4 + g];
+    for (int j = 0; j < 4; j++) sa[j] = bp[sa_base + sa_j[j]];
 #pragma unroll
     for (int t = 0; t < NT; t++) sb[t] = bp[kBigBsf + (t * 16 + r16) * 4 + g];
     v4i n0 = *(const v4i*)(bp + brd0);
@@ -928,7 +931,7 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   const uint32_t arow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
   const uint32_t wrows = l1 ? 2u * (uint32_t)I : (uint32_t)H;
   const uint8_t* W = l1 ? p.w1 + (size_t)e * wrows * arow : p.w2 + (size_t)e * wrows * arow;
-  const uint8_t* Ws = l1 ? p.w1_sf + (size_t)e * wrows * srow : p.w2_sf + (size_t)e * wrows * srow;
+  const uint8_t* Ws = l1 ? p.w1_sf_km + (size_t)e * wrows * srow : p.w2_sf_km + (size_t)e * wrows * srow;
   int rb[4];  // first weight row of each 16-row block of this wave
   if (l1) {
     const int i0 = nb * 128 + wave * 32;
@@ -944,7 +947,15 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   const rsrc_t rW = make_rsrc(W, wrows * arow);
   const rsrc_t rWs = make_rsrc(Ws, wrows * srow);
   const uint32_t a_off = (uint32_t)r16 * arow + (uint32_t)g * 16;
-  const uint32_t as_off = (uint32_t)(rb[lane >> 4] + r16) * srow;
+  // K-major weight scales: lane l fetches tile rows 4l..4l+3 of the wave's block
+  // (L1: gate rows of the tile for l < 32, up rows for l >= 32)
+  const uint32_t as_off = l1 ? (uint32_t)((lane < 32 ? 0 : I) + nb * 128 + 4 * (lane & 31))
+                             : (uint32_t)(nb * 256 + 4 * lane);
+  // ... and reads the byte of block g for weight row block j at sa_base + sa_j[j]
+  const uint32_t sa_base = (uint32_t)(kBigAsf + g * 256 + r16 + (l1 ? wave * 32 : wave * 64));
+  int sa_j[4];
+#pragma unroll
+  for (int j = 0; j < 4; j++) sa_j[j] = l1 ? (j >> 1) * 128 + (j & 1) * 16 : j * 16;
 
   // routed rows of the tile (rows past the expert repeat its first row / read
   // padding): fill instruction i of this wave covers rows 8*(RP*wave + i) + (l%16)/2
@@ -983,8 +994,8 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   if (NT == 8 ? wave >= 2 : wave >= 1) xs_off = 0x80000000u;
 
   v4f acc[4][NT];
-  big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, rX, xoff, brd0, brd1, rXs, xs_off, nk, wave,
-                lane);
+  big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, wrows, sa_base, sa_j, rX, xoff, brd0, brd1,
+                rXs, xs_off, nk, wave, lane);
 
   if (!active) return;
   if (l1) {
@@ -1537,6 +1548,36 @@ __global__ __launch_bounds__(kThreads, 2) void moe_ffn_kernel(KParams p) {
 }
 
 int max_block_m(int recipe) { return recipe == 2 ? 128 : 64; }
+
+// ---------------------------------------------------------------------------
+// Weight-scale transform: a workgroup re-orders one 64-row x 64-block tile of
+// one expert's scale matrix through LDS (row-major in, K-major out).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void transform_scales_kernel(const uint8_t* __restrict__ src,
+                                                                uint8_t* __restrict__ dst, int64_t rows, int64_t kb) {
+  __shared__ uint8_t tile[64][65];
+  const int64_t e = blockIdx.z;
+  const int64_t r0 = (int64_t)blockIdx.y * 64, b0 = (int64_t)blockIdx.x * 64;
+  const uint8_t* s = src + e * rows * kb;
+  uint8_t* d = dst + e * rows * kb;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i >> 6, b = i & 63;
+    tile[r][b] = (r0 + r < rows && b0 + b < kb) ? s[(r0 + r) * kb + b0 + b] : (uint8_t)0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int b = i >> 6, r = i & 63;
+    if (r0 + r < rows && b0 + b < kb) d[(b0 + b) * rows + r0 + r] = tile[r][b];
+  }
+}
+
+hipError_t launch_transform_scales(const uint8_t* src, uint8_t* dst, int64_t E, int64_t rows, int64_t kb,
+                                   hipStream_t stream) {
+  if ((kb + 63) / 64 > 0x7FFFFFFF || (rows + 63) / 64 > 65535 || E > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((kb + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)E);
+  hipLaunchKernelGGL(transform_scales_kernel, grid, dim3(256), 0, stream, src, dst, rows, kb);
+  return hipGetLastError();
+}
 
 template <int RECIPE, int BM>
 static hipError_t launch_one(int grid, const KParams& p, hipStream_t stream) {

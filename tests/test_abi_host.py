@@ -118,3 +118,20 @@ def test_forward_rejects_small_workspace():
     rc = mf.lib().moe_ffn_forward(ctypes.byref(prob), ctypes.byref(a), ctypes.c_void_p(1 << 20),
                                   ctypes.c_size_t(need - 1), None)
     assert rc == mf.ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(src=None), mf.ERR_INVALID_ARG),
+    (dict(dst=None), mf.ERR_INVALID_ARG),
+    (dict(rows=6), mf.ERR_INVALID_ARG),        # rows not a multiple of 4
+    (dict(kb=0), mf.ERR_INVALID_ARG),
+    (dict(E=0), mf.ERR_INVALID_ARG),
+    (dict(dst=4098), mf.ERR_INVALID_ARG),      # dst not 4-byte aligned
+])
+def test_transform_weight_scales_argument_checks(kw, code):
+    a = dict(src=4096, dst=8192, E=2, rows=8, kb=3)
+    a.update(kw)
+    rc = mf.lib().moe_ffn_transform_weight_scales(
+        None if a["src"] is None else ctypes.c_void_p(a["src"]), None if a["dst"] is None else ctypes.c_void_p(a["dst"]),
+        a["E"], a["rows"], a["kb"], None)
+    assert rc == code

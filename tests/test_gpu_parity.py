@@ -232,3 +232,39 @@ def test_graph_replay_changed_inputs_matches_eager():
         _check_tables(run, q, q["T"])
         ref, allow = oracle_y_band(q, False, q["clamp"])
         assert_y_parity(run.y_float(), ref, allow, 2e-2, f"replay {r}")
+
+
+@pytest.mark.parametrize("E,rows,kb", [(3, 8, 3), (2, 256, 12), (2, 4096, 224), (1, 7168, 64)])
+def test_transform_weight_scales_bitexact(E, rows, kb):
+    import mixture_experts_ffn_histogram_amd as mf
+    rng = np.random.default_rng(rows + kb)
+    src = rng.integers(0, 256, size=(E, rows, kb), dtype=np.uint8)
+    s = torch.from_numpy(src).cuda()
+    d = torch.full((E, kb, rows), 0xA5, dtype=torch.uint8, device="cuda")
+    log(f"transform E={E} rows={rows} kb={kb}")
+    mf.transform_weight_scales(s, d, E, rows, kb)
+    torch.cuda.synchronize()
+    assert np.array_equal(d.cpu().numpy(), np.ascontiguousarray(src.transpose(0, 2, 1)))
+
+
+def test_large_call_without_kmajor_scales_uses_64_row_tiles(monkeypatch):
+    # the 128-row tiles need the K-major weight-scale copies; without them the
+    # call runs on 64-row tiles and must give the same answer
+    monkeypatch.setenv("MOE_FFN_BLOCK_M", "128")
+    cfg = _small_cfg(synth.RECIPE_FP8_FP4, 520, 1024, 512, 3, 3, "softmax", seed=5)
+    p = synth.make_problem(cfg, threads=8)
+    log("block 128 requested, no K-major scales")
+    run = Runner(p, kmajor=False)
+    run.run()
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    _check_tables(run, p, p["T"])
+    ref, allow = oracle_y_band(p, False, p["clamp"])
+    assert_y_parity(run.y_float(), ref, allow, 2e-2, "no K-major scales")
+    y64 = run.y.clone()
+    run_km = Runner(p)
+    run_km.run()
+    torch.cuda.synchronize()
+    assert int(run_km.status.item()) == 0
+    assert_y_parity(run_km.y_float(), ref, allow, 2e-2, "K-major scales")
+    log(f"  64-row vs 128-row tiles: {int((y64 != run_km.y).sum())} of {y64.numel()} y elements differ in the last bit")
