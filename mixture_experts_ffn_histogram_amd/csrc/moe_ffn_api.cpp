@@ -208,10 +208,15 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   const long bm_env = env_long("MOE_FFN_BLOCK_M", 0);  // tuning override: 16, 32, 64 or 128
   if ((bm_env == 16 || bm_env == 32 || bm_env == 64 || bm_env == 128) && bm_env <= moeffn::max_block_m(recipe))
     bm = (int)bm_env;
-  if (bm == 128 && (!big_ok || !km)) bm = 64;  // the 128-row tiles read the K-major weight scales
+  if (bm == 128 && (!big_ok || !km || L.hsg == L.xsg)) bm = 64;  // the 128-row tiles read the K-major weight scales
   if (env_long("MOE_FFN_LOG", 0) > 0)
     std::fprintf(stderr, "moe_ffn: T=%lld recipe=%d grid=%d (CUs %d, reserve %d, cap %d) block_m=%d\n",
                  (long long)T, recipe, grid, cus, reserve, a->max_cus, bm);
+  if (bm == 128) {
+    k.xsg = reinterpret_cast<uint32_t*>(ws + L.xsg);
+    k.hsg = reinterpret_cast<uint32_t*>(ws + L.hsg);
+    k.sg_rows = (int32_t)L.h_rows;
+  }
   const hipError_t err = moeffn::launch_forward(recipe, bm, grid, k, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }

@@ -44,6 +44,10 @@ struct KParams {
   uint8_t* h;
   uint8_t* h_sf;
   float* o;
+  // 128-row tiles only (else null): stage-major scale copies, sg_rows rows each
+  uint32_t* xsg;
+  uint32_t* hsg;
+  int32_t sg_rows;
 };
 
 // Launches the persistent kernel for `recipe` with token block `bm` on `grid`

@@ -268,6 +268,10 @@ __device__ void scatter_range(const KParams& p, Shared& sh, WaveCounters& wcnt, 
       if (to_global) {
         p.r2s[row] = s;
         p.s2r[s] = row;
+        if (p.xsg) {  // the token's activation scales, one dword per K stage, to the row's column
+          const uint32_t* src = reinterpret_cast<const uint32_t*>(p.x_sf) + (size_t)(s / p.k) * (size_t)(p.H >> 7);
+          for (int st = 0; st < (p.H >> 7); st++) p.xsg[(size_t)st * p.sg_rows + row] = src[st];
+        }
         if (p.out_r2s) p.out_r2s[row] = s;
         if (p.out_s2r) p.out_s2r[s] = row;
       }
@@ -773,6 +777,20 @@ __device__ void wave_tile(const KParams& p, const Shared& sh, const int* lr2s, b
   }
 }
 
+// DPP rotate by 8 lanes inside each 16-lane row.
+__device__ __forceinline__ int dpp_ror8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
+
+// lanes 0-7 of each 16-lane row take x0 (par 0) / rotated x0 (par 1); lanes 8-15 rotated x1 / x1
+__device__ __forceinline__ v4i line_shuffle(const v4i& x0, const v4i& x1, int par, bool lo) {
+  v4i r;
+#pragma unroll
+  for (int d = 0; d < 4; d++) {
+    const int rot = dpp_ror8(par == 0 ? x1[d] : x0[d]);  // every lane executes the DPP move
+    r[d] = par == 0 ? (lo ? x0[d] : rot) : (lo ? rot : x1[d]);
+  }
+  return r;
+}
+
 // ---------------------------------------------------------------------------
 // 128-row workgroup tiles for e4m3 rows x e2m1 weights (the MFMA-bound
 // regime).  4 waves x 64 weight rows x 128 routed rows, acc[j][t] for weight
@@ -811,7 +829,8 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
                                           v4f (&acc)[4][NT], rsrc_t rW, uint32_t a_off, const uint32_t (&a_soff)[4],
                                           rsrc_t rWs, uint32_t as_off, uint32_t ws_stride, uint32_t sa_base,
                                           const int (&sa_j)[4], rsrc_t rX, const uint32_t (&xoff)[4],
-                                          uint32_t brd0, uint32_t brd1, rsrc_t rXs, uint32_t xs_off, int nk, int wave,
+                                          uint32_t brd0, uint32_t brd1, rsrc_t rXs, uint32_t xs_off, uint32_t xs_stride,
+                                          int nk, int wave,
                                           int lane) {
   constexpr int RP = big_row_pieces<NT>();
   const int g = lane >> 4, r16 = lane & 15;
@@ -822,9 +841,13 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
     for (int t = 0; t < NT; t++) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
   v4i ar[kBigP][4];
 
+  // A stage past the end (the ring runs kBigP stages ahead) is fetched from
+  // an offset past the buffer's end: the load returns zeros without a memory
+  // access and still counts as one vector-memory operation for the waits.
   auto load_a = [&](int slot, int s) {
+    const uint32_t voff = s < nk ? a_off : kBufDead;
 #pragma unroll
-    for (int j = 0; j < 4; j++) ar[slot][j] = buf_load16(rW, a_off, a_soff[j] + (uint32_t)s * 64);
+    for (int j = 0; j < 4; j++) ar[slot][j] = buf_load16(rW, voff, a_soff[j] + (uint32_t)s * 64);
   };
   // Stage s into ring buffer `buf`: 2*NT x 1 KB of routed-row bytes, whole
   // 128-byte lines: instruction q holds rows 8q..8q+7, its lane l row
@@ -838,11 +861,13 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
   // as [block][tile row].
   auto dma = [&](int s, int buf) {
     uint8_t* bp = BUF(buf);
+    const bool live = s < nk;
 #pragma unroll
-    for (int i = 0; i < RP; i++) buf_load_lds16(rX, bp + (wave * RP + i) * 1024, xoff[i], (uint32_t)s * 128);
+    for (int i = 0; i < RP; i++)
+      buf_load_lds16(rX, bp + (wave * RP + i) * 1024, live ? xoff[i] : kBufDead, (uint32_t)s * 128);
     const int scopy = NT == 8 ? ((wave >> 1) * kBigBM + (wave & 1) * 64) : wave * 64;
-    buf_load_lds4(rXs, bp + kBigBsf + scopy * 4, xs_off, (uint32_t)s * 4);
-    buf_load_lds4(rWs, bp + kBigAsf + wave * 256, as_off, (uint32_t)(4 * s + wave) * ws_stride);
+    buf_load_lds4(rXs, bp + kBigBsf + scopy * 4, live ? xs_off : kBufDead, (uint32_t)s * xs_stride);
+    buf_load_lds4(rWs, bp + kBigAsf + wave * 256, live ? as_off : kBufDead, (uint32_t)(4 * s + wave) * ws_stride);
   };
   auto compute = [&](int slot, int buf) {
     const uint8_t* bp = BUF(buf);
@@ -879,11 +904,11 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
   __builtin_amdgcn_sched_barrier(0);
   dma(0, 0);
   __builtin_amdgcn_sched_barrier(0);
-  load_a(1, 1 < nk ? 1 : nk - 1);
+  load_a(1, 1);
   __builtin_amdgcn_sched_barrier(0);
-  dma(1 < nk ? 1 : nk - 1, 1);
+  dma(1, 1);
   __builtin_amdgcn_sched_barrier(0);
-  load_a(2, 2 < nk ? 2 : nk - 1);
+  load_a(2, 2);
   __builtin_amdgcn_sched_barrier(0);
   int s0 = 0;
   for (; s0 + kBigP <= nk; s0 += kBigP) {
@@ -892,10 +917,10 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
       const int s = s0 + u;
       MOEFFN_WAIT_VMCNT(big_wait<NT>());  // this wave's fill of stage s has landed
       __builtin_amdgcn_s_barrier();       // ... and every other wave's
-      dma(s + kBigD < nk ? s + kBigD : nk - 1, (u + kBigD) % kBigNB);
+      dma(s + kBigD, (u + kBigD) % kBigNB);
       __builtin_amdgcn_sched_barrier(0);
       compute(u, u);
-      load_a(u, s + kBigP < nk ? s + kBigP : nk - 1);
+      load_a(u, s + kBigP);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -966,24 +991,24 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   uint32_t xoff[4] = {0u, 0u, 0u, 0u}, xs_off;
   if (l1) {
     rX = make_rsrc(p.x, (uint32_t)p.T * (uint32_t)H);
-    rXs = make_rsrc(p.x_sf, (uint32_t)p.T * (uint32_t)(H / 32));
+    rXs = make_rsrc(p.xsg, (uint32_t)(H / 128) * (uint32_t)p.sg_rows * 4u);
 #pragma unroll
     for (int i = 0; i < RP; i++) {
       const int q = wave * RP + i, m = 8 * q + c8;
       const uint32_t tok = (uint32_t)(route_slot(p, nullptr, false, row0 + (m < nrows ? m : 0)) / p.k);
       xoff[i] = tok * (uint32_t)H + (uint32_t)((((lane & 1) ^ (q & 1)) * 4 + g) * 16);
     }
-    xs_off = (uint32_t)(route_slot(p, nullptr, false, row0 + (ms < nrows ? ms : 0)) / p.k) * (uint32_t)(H / 32);
+    xs_off = (uint32_t)(row0 + ms) * 4u;
   } else {
     const uint32_t rows_end = (uint32_t)(row0 + kBigBM);  // h is padded by kMaxBM rows
     rX = make_rsrc(p.h, rows_end * (uint32_t)I);
-    rXs = make_rsrc(p.h_sf, rows_end * (uint32_t)(I / 32));
+    rXs = make_rsrc(p.hsg, (uint32_t)(I / 128) * (uint32_t)p.sg_rows * 4u);
 #pragma unroll
     for (int i = 0; i < RP; i++) {
       const int q = wave * RP + i;
       xoff[i] = (uint32_t)(row0 + 8 * q + c8) * (uint32_t)I + (uint32_t)((((lane & 1) ^ (q & 1)) * 4 + g) * 16);
     }
-    xs_off = (uint32_t)(row0 + ms) * (uint32_t)(I / 32);
+    xs_off = (uint32_t)(row0 + ms) * 4u;
   }
   const uint32_t brd0 = (uint32_t)(((r16 >> 3) * 64 + g * 16 + 2 * (r16 & 7) + (0 ^ (r16 >> 3))) * 16);
   const uint32_t brd1 = (uint32_t)(((r16 >> 3) * 64 + g * 16 + 2 * (r16 & 7) + (1 ^ (r16 >> 3))) * 16);
@@ -991,11 +1016,11 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   // reads past the end of the buffer instead: that load returns zeros without
   // a memory access (each dword it would fetch is a cache line of its own),
   // and every wave still issues the same count.
-  if (NT == 8 ? wave >= 2 : wave >= 1) xs_off = 0x80000000u;
+  if (NT == 8 ? wave >= 2 : wave >= 1) xs_off = kBufDead;
 
   v4f acc[4][NT];
   big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, wrows, sa_base, sa_j, rX, xoff, brd0, brd1,
-                rXs, xs_off, nk, wave, lane);
+                rXs, xs_off, (uint32_t)p.sg_rows * 4u, nk, wave, lane);
 
   if (!active) return;
   if (l1) {
@@ -1023,7 +1048,11 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
           for (int j = 0; j < 4; j++) word |= f32_to_e4m3(__builtin_amdgcn_ldexpf(hv[hh * 4 + j], -E)) << (8 * j);
           stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
         }
-        if (g == 0) stg1(p.h_sf + row * (size_t)(I / 32) + (size_t)(i0 / 32), (uint8_t)(E + 127));
+        if (g == 0) {
+          stg1(p.h_sf + row * (size_t)(I / 32) + (size_t)(i0 / 32), (uint8_t)(E + 127));
+          // byte `wave` of stage nb's dword of the row (block i0/32 = 4 nb + wave)
+          stg1(reinterpret_cast<uint8_t*>(p.hsg + (size_t)nb * p.sg_rows + row) + wave, (uint8_t)(E + 127));
+        }
       }
     }
   } else {
@@ -1055,19 +1084,6 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
 #ifndef MOEFFN_W4_PP
 #define MOEFFN_W4_PP 2
 #endif
-__device__ __forceinline__ int dpp_ror8(int v) { return __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, false); }
-
-// lanes 0-7 of each 16-lane row take x0 (par 0) / rotated x0 (par 1); lanes 8-15 rotated x1 / x1
-__device__ __forceinline__ v4i line_shuffle(const v4i& x0, const v4i& x1, int par, bool lo) {
-  v4i r;
-#pragma unroll
-  for (int d = 0; d < 4; d++) {
-    const int rot = dpp_ror8(par == 0 ? x1[d] : x0[d]);  // every lane executes the DPP move
-    r[d] = par == 0 ? (lo ? x0[d] : rot) : (lo ? rot : x1[d]);
-  }
-  return r;
-}
-
 template <int BM>
 __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s, bool local, bool l1, int e, int mb,
                              int blk) {
@@ -1403,23 +1419,28 @@ __device__ __forceinline__ void phase_big_tiles(const KParams& p, Shared& sh, co
 }
 
 // ---------------------------------------------------------------------------
-// C: combine.  Each wave takes whole tokens: it reads the token's k row
-// indices and weights once, then streams the k fp32 rows of o in 256-column
-// slices (64 lanes x 4 floats), two slices in flight, accumulating in slot
-// order j = 0..k-1 with fused multiply-adds.
+// C: combine.  A unit of work is one token x 1024 columns (units spread
+// evenly over the waves even when T is not a multiple of the wave count): the
+// wave reads the token's k row indices and weights, then streams the k fp32
+// rows of o in 256-column slices (64 lanes x 4 floats), two slices in flight,
+// accumulating in slot order j = 0..k-1 with fused multiply-adds.
 // ---------------------------------------------------------------------------
 __device__ void phase_combine(const KParams& p) {
   const int lane = threadIdx.x & 63;
   const int H = p.H, k = p.k;
   const int nw = gridDim.x * 4;
-  for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < p.T; t += nw) {
+  const int nc = (H + 1023) >> 10;  // 1024-column units per token
+  const int units = p.T * nc;
+  for (int u = blockIdx.x * 4 + (threadIdx.x >> 6); u < units; u += nw) {
+    const int t = u / nc, cu = u - t * nc;
     // lane j < k holds slot j's row and weight
     const int myrow = lane < k ? p.s2r[(size_t)t * k + lane] : -1;
     const float myw = lane < k ? p.tw[(size_t)t * k + lane] : 0.f;
-    for (int c0 = 0; c0 < H; c0 += 512) {
+    const int cend = min(H, (cu + 1) << 10);
+    for (int c0 = cu << 10; c0 < cend; c0 += 512) {
       const int ca = c0 + lane * 4;
       const int cb = c0 + 256 + lane * 4;
-      const bool va = ca < H, vb = cb < H;
+      const bool va = ca < cend, vb = cb < cend;
       v4f acca = {0.f, 0.f, 0.f, 0.f}, accb = {0.f, 0.f, 0.f, 0.f};
       for (int j0 = 0; j0 < k; j0 += 8) {
         v4f oa[8], ob[8];

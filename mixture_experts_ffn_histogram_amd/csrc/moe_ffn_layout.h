@@ -40,7 +40,7 @@ static_assert(offsetof(Ctrl, xq) == 44, "layout change must be deliberate");
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ctrl, counts, offsets, hist, r2s, s2r, h, h_sf, o, total;
+  size_t ctrl, counts, offsets, hist, r2s, s2r, h, h_sf, o, xsg, hsg, total;
   int64_t chunk_slots;   // slots per routing chunk
   int64_t max_slots;     // max_tokens * k
   int64_t h_rows;        // rows of h (max_slots + kMaxBM padding)
@@ -69,6 +69,13 @@ inline Layout make_layout(int64_t max_tokens, int64_t H, int64_t I, int64_t E, i
   L.h = off;       off = align_up(off + (size_t)L.h_rows * (size_t)L.h_row_bytes, A);
   L.h_sf = off;    off = align_up(off + (size_t)L.h_rows * (size_t)L.h_sf_row_bytes, A);
   L.o = off;       off = align_up(off + (size_t)(L.max_slots > 0 ? L.max_slots : 1) * (size_t)L.o_row_bytes, A);
+  // e4m3 x e2m1 with H and I multiples of 128: stage-major copies of the
+  // activation scales of the routed rows, xsg[H/128][h_rows] and
+  // hsg[I/128][h_rows] (one dword = the 4 e8m0 bytes of a 128-element K
+  // stage), so that a stage's scales of consecutive routed rows are contiguous
+  const bool sg = recipe == 2 && H % 128 == 0 && I % 128 == 0;
+  L.xsg = off;     off = align_up(off + (sg ? (size_t)(H / 128) * (size_t)L.h_rows * 4 : 0), A);
+  L.hsg = off;     off = align_up(off + (sg ? (size_t)(I / 128) * (size_t)L.h_rows * 4 : 0), A);
   L.total = off;
   return L;
 }
