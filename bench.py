@@ -10,7 +10,9 @@ Prints ONE JSON line: headline workload T=8192 with Zipf(1.2) routing and
 10% empty experts (MFMA-bound: useful TFLOP/s and fraction of the dense FP8
 MFMA peak), plus the T=128 weight-streaming workload (HBM-bound: fraction of
 the 8 TB/s HBM peak) under "secondary", the roofline of the kernel and the
-CPU oracle timed on a bounded token sample.
+CPU oracle timed on a bounded token sample.  The pre-dispatch activation
+quantisation (bf16 x of the headline shape -> e4m3 + e8m0) is timed under
+"quantize" (HBM-bound).
 """
 from __future__ import annotations
 
@@ -129,6 +131,40 @@ def run_workload(name: str, steps: int, warmup: int, threads: int, log):
     return {"p": p, "cfg": cfg, "ms": ms, "R": R, "active": active, "flops": flops, "bytes": abytes}
 
 
+def run_quantize(T: int, H: int, steps: int, warmup: int, log):
+    """Pre-dispatch activation quantisation (bf16 [T, H] -> e4m3 + e8m0 per 1x32), HBM-bound."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_histogram_amd as mf
+    from mixture_experts_ffn_histogram_amd import synth
+
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(synth.activations_bf16(T, H, seed=T).view(np.int16)).to(dev)
+    q = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    sf = torch.empty((T, H // 32), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        mf.quantize_activations(x, q, sf, stream)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        mf.quantize_activations(x, q, sf, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    nbytes = T * H * 2 + T * H + T * (H // 32)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] quantize T={T} H={H}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s")
+    return {"workload": f"quantize_bf16_to_e4m3_T{T}_H{H}", "us_per_call": round(ms * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "kernel": "quantize_act_kernel",
+                         "work_per_launch": f"{nbytes} algorithmic bytes (2 B read + 1 B + 1/32 B written "
+                                            "per element)"}}
+
+
 def cpu_baseline(p, clamp: float, target_s: float, log):
     """The CPU oracle as it stands, per-token path, on a bounded token sample."""
     import numpy as np
@@ -164,6 +200,8 @@ def main() -> int:
     ap.add_argument("--secondary", default="deepseek_fp8xfp4_T128")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-quantize", action="store_true",
+                    help="skip the pre-dispatch activation quantisation timing")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (read + write) a few times, for scaling the "
@@ -229,6 +267,8 @@ def main() -> int:
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic_from_profiles(args.secondary),
                          "kernel": "moe_ffn_kernel<2,16>",
                          "work_per_launch": f"{sec['bytes']} algorithmic bytes ({sec['active']} active experts)"}}
+    if not args.no_quantize:
+        out["quantize"] = run_quantize(p["T"], p["H"], args.steps, args.warmup, log)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, main_r["cfg"].clamp, args.cpu_seconds, log)
     print(json.dumps(out), flush=True)

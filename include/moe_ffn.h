@@ -138,6 +138,31 @@ int moe_ffn_forward(const moe_ffn_problem* problem, const moe_ffn_args* args,
 int moe_ffn_transform_weight_scales(const uint8_t* src, uint8_t* dst, int64_t num_experts, int64_t rows,
                                     int64_t k_blocks, void* stream);
 
+/* Pre-dispatch activation quantisation, the step right before the forward
+   ("[Blackwell] Reserve SMs for DeepGEMM MegaMoE grid barriers", Fix section:
+   pre-dispatch runs before the kernel call; its digest, key-code section: the
+   buffer fetch and pre-dispatch quantisation precede the call).  The pages do
+   not state its arithmetic; it applies the forward's own 1x32 re-quantisation
+   rule to bf16 activations:
+     for every 32-element block b of a row (blocks along H):
+       E = smallest integer with amax(|x|) <= 448 * 2^E, clamped to
+           [-127, 127]; E = 0 for an all-zero block;
+       x_sf[b] = E + 127;
+       x_e4m3[i] = E4M3FN code of x[i] * 2^-E, rounded to nearest even,
+                   saturating (never NaN).
+   x_bf16: [num_tokens, hidden] bf16 bit patterns (device, 16-byte aligned),
+   finite values (a block holding inf or NaN gets unspecified codes);
+   x_e4m3: [num_tokens, hidden] bytes (device, 8-byte aligned);
+   x_sf: [num_tokens, hidden/32] e8m0 bytes (device).  The outputs are exactly
+   the x / x_sf inputs of moe_ffn_forward for the e4m3 recipes.  hidden must
+   be a positive multiple of 32 (else MOE_FFN_ERR_UNSUPPORTED); num_tokens = 0
+   is a no-op.  Enqueued on `stream` (a hipStream_t; NULL = default stream);
+   asynchronous, allocates nothing, capturable.  Returns
+   MOE_FFN_ERR_INVALID_ARG for negative sizes, null or misaligned pointers
+   with num_tokens > 0, MOE_FFN_ERR_HIP when the launch fails. */
+int moe_ffn_quantize_activations(const void* x_bf16, int64_t num_tokens, int64_t hidden, void* x_e4m3,
+                                 uint8_t* x_sf, void* stream);
+
 /* Text of a return or status code (static string). */
 const char* moe_ffn_strerror(int code);
 

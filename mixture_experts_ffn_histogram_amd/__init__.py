@@ -59,7 +59,7 @@ class WorkspaceView(ctypes.Structure):
 
 EXPORTS = ("moe_ffn_get_workspace_size", "moe_ffn_get_token_alignment", "moe_ffn_forward",
            "moe_ffn_strerror", "moe_ffn_launch_size", "moe_ffn_get_workspace_view",
-           "moe_ffn_transform_weight_scales")
+           "moe_ffn_transform_weight_scales", "moe_ffn_quantize_activations")
 
 _lib = None
 
@@ -87,6 +87,8 @@ def lib():
         L.moe_ffn_get_workspace_view.restype = ctypes.c_int
         L.moe_ffn_transform_weight_scales.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
         L.moe_ffn_transform_weight_scales.restype = ctypes.c_int
+        L.moe_ffn_quantize_activations.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P]
+        L.moe_ffn_quantize_activations.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -146,6 +148,20 @@ def transform_weight_scales(src, dst, num_experts: int, rows: int, k_blocks: int
     rc = lib().moe_ffn_transform_weight_scales(_ptr(src), _ptr(dst), int(num_experts), int(rows), int(k_blocks),
                                                ctypes.c_void_p(stream.cuda_stream))
     _check(rc, "moe_ffn_transform_weight_scales")
+
+
+def quantize_activations(x_bf16, x_e4m3, x_sf, stream=None) -> None:
+    """Enqueue moe_ffn_quantize_activations: bf16 x [T, H] (int16 or bfloat16 device tensor) ->
+    e4m3 codes x_e4m3 [T, H] and e8m0 scales x_sf [T, H/32] (uint8 device tensors)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    T, H = int(x_bf16.shape[0]), int(x_bf16.shape[1])
+    assert x_bf16.is_contiguous() and x_e4m3.is_contiguous() and x_sf.is_contiguous()
+    assert x_bf16.element_size() == 2 and tuple(x_e4m3.shape) == (T, H) and x_sf.numel() == T * (H // 32)
+    rc = lib().moe_ffn_quantize_activations(_ptr(x_bf16), T, H, _ptr(x_e4m3), _ptr(x_sf),
+                                            ctypes.c_void_p(stream.cuda_stream))
+    _check(rc, "moe_ffn_quantize_activations")
 
 
 def kmajor_weight_scales(w1_sf, w2_sf, num_experts: int, hidden: int, intermediate: int, stream=None):

@@ -116,6 +116,19 @@ int moe_ffn_transform_weight_scales(const uint8_t* src, uint8_t* dst, int64_t nu
   return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 
+int moe_ffn_quantize_activations(const void* x_bf16, int64_t num_tokens, int64_t hidden, void* x_e4m3,
+                                 uint8_t* x_sf, void* stream) {
+  if (num_tokens < 0 || hidden <= 0) return MOE_FFN_ERR_INVALID_ARG;
+  if (hidden % 32 != 0) return MOE_FFN_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return MOE_FFN_OK;
+  if (!x_bf16 || !x_e4m3 || !x_sf) return MOE_FFN_ERR_INVALID_ARG;
+  if (!aligned16(x_bf16) || (reinterpret_cast<uintptr_t>(x_e4m3) & 7u) != 0) return MOE_FFN_ERR_INVALID_ARG;
+  if (num_tokens > (int64_t(1) << 40) / hidden) return MOE_FFN_ERR_UNSUPPORTED;
+  const hipError_t e = moeffn::launch_quantize_act(static_cast<const uint16_t*>(x_bf16), static_cast<uint8_t*>(x_e4m3),
+                                                   x_sf, num_tokens * hidden, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
 const char* moe_ffn_strerror(int code) {
   switch (code) {
     case MOE_FFN_OK: return "ok";

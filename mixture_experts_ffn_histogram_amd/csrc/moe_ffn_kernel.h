@@ -61,4 +61,7 @@ hipError_t launch_transform_scales(const uint8_t* src, uint8_t* dst, int64_t E, 
 // Largest token block the recipe supports (register budget of the A ring).
 int max_block_m(int recipe);
 
+// bf16 -> e4m3 + e8m0 per 1x32 block over n_elems elements (a multiple of 32).
+hipError_t launch_quantize_act(const uint16_t* x, uint8_t* q, uint8_t* sf, int64_t n_elems, hipStream_t stream);
+
 }  // namespace moeffn

@@ -216,6 +216,17 @@ def activations(cfg: Config, T: int | None = None):
     return x, x_sf
 
 
+def activations_bf16(T: int, H: int, seed: int) -> np.ndarray:
+    """bf16 activations [T, H] (uint16 bit patterns) for the pre-dispatch quantisation:
+    N(0, 1) rows times a per-token log-normal gain (sigma 1), with one element
+    in 500 boosted 16x (outlier channels), so blocks span a wide range of scales."""
+    rng = _rng(seed, _TID["x"], T, H)
+    v = rng.standard_normal(size=(T, H), dtype=np.float32)
+    v *= np.exp(rng.standard_normal(size=(T, 1))).astype(np.float32)
+    v[rng.random(size=(T, H)) < 0.002] *= np.float32(16.0)
+    return torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
 def make_problem(cfg: Config, T: int | None = None, threads: int = 8, weights=None) -> dict:
     """All inputs of one forward call as numpy arrays (plus the dims)."""
     T = cfg.T if T is None else T

@@ -71,6 +71,7 @@ def lib():
             ("oracle_forward_tokens_band", ctypes.c_int, [P] + [P] * 8 + [P, i64, P, d, P]),
             ("oracle_ffn_row", ctypes.c_int, [P, P, P, i64, i64, P, P, P, P, P, P, P, P, P, P, d, P]),
             ("oracle_num_threads", ctypes.c_int, []),
+            ("oracle_quantize_act", ctypes.c_int, [P, i64, i64, P, P]),
         ]:
             fn = getattr(L, name)
             fn.restype = res
@@ -210,6 +211,19 @@ def ffn_row(p: dict, t: int, e: int, clamp: float, rho: float = 0.0):
     if rc < 0:
         raise RuntimeError(f"oracle_ffn_row failed: {rc}")
     return {"c": c, "h": h, "hq": hq, "h_codes": codes, "h_sf": hsf, "o": o, "delta": delta}
+
+
+def quantize_act(x_bits: np.ndarray):
+    """Pre-dispatch quantisation of bf16 activations (uint16 bit patterns [T, H], H % 32 == 0):
+    returns (e4m3 codes uint8 [T, H], e8m0 scales uint8 [T, H/32])."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    T, H = x.shape
+    codes = np.zeros((T, H), np.uint8)
+    sf = np.zeros((T, H // 32), np.uint8)
+    rc = lib().oracle_quantize_act(_ptr(x), int(T), int(H), _ptr(codes), _ptr(sf))
+    if rc < 0:
+        raise RuntimeError(f"oracle_quantize_act failed: {rc}")
+    return codes, sf
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

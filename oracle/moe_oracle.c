@@ -550,6 +550,39 @@ int oracle_ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
                    rho, NULL, delta_out);
 }
 
+/* ------------------------------------------------------------------------ */
+/* Pre-dispatch activation quantisation: bf16 activations -> e4m3 codes and */
+/* one e8m0 scale per 1x32 block along the hidden dimension, the x / x_sf   */
+/* the forward consumes.  The pages place the step before the kernel call   */
+/* ("[Blackwell] Reserve SMs for DeepGEMM MegaMoE grid barriers", Fix       */
+/* section; its digest, key-code section) without its arithmetic; the       */
+/* reading is the forward's own O5 rule on the exact bf16 values: for each  */
+/* block, E = oracle_scale_exp(max |x|), sf = E + 127, and each code is the */
+/* E4M3FN pattern of round_e4m3_sat(x * 2^-E) (the scaling by 2^-E is exact */
+/* in double).  Rows are independent; parity status: pinned (tests).        */
+/* ------------------------------------------------------------------------ */
+int oracle_quantize_act(const uint16_t* x, int64_t T, int64_t H, uint8_t* codes, uint8_t* sf) {
+    int64_t t, b;
+    int i;
+    if (T < 0 || H <= 0 || H % 32 != 0 || (T > 0 && (!x || !codes || !sf))) return OR_BAD_ARG;
+    for (t = 0; t < T; t++) {
+        for (b = 0; b < H / 32; b++) {
+            const uint16_t* xb = x + t * H + b * 32;
+            double amax = 0.0;
+            int E;
+            for (i = 0; i < 32; i++) {
+                const double a = fabs(oracle_dec_bf16(xb[i]));
+                if (a > amax) amax = a;
+            }
+            E = oracle_scale_exp(amax);
+            sf[t * (H / 32) + b] = (uint8_t)(E + 127);
+            for (i = 0; i < 32; i++)
+                codes[t * H + b * 32 + i] = oracle_enc_e4m3(oracle_round_e4m3_sat(ldexp(oracle_dec_bf16(xb[i]), -E)));
+        }
+    }
+    return OR_OK;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

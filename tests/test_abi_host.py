@@ -135,3 +135,21 @@ def test_transform_weight_scales_argument_checks(kw, code):
         None if a["src"] is None else ctypes.c_void_p(a["src"]), None if a["dst"] is None else ctypes.c_void_p(a["dst"]),
         a["E"], a["rows"], a["kb"], None)
     assert rc == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=48), mf.ERR_UNSUPPORTED),          # hidden not a multiple of 32
+    (dict(H=0), mf.ERR_INVALID_ARG),
+    (dict(T=-1), mf.ERR_INVALID_ARG),
+    (dict(T=0, x=None, q=None, sf=None), mf.OK),  # no-op, no device work
+    (dict(x=None), mf.ERR_INVALID_ARG),
+    (dict(sf=None), mf.ERR_INVALID_ARG),
+    (dict(x=4104), mf.ERR_INVALID_ARG),        # x not 16-byte aligned
+    (dict(q=4100), mf.ERR_INVALID_ARG),        # codes not 8-byte aligned
+])
+def test_quantize_activations_argument_checks(kw, code):
+    a = dict(x=4096, T=4, H=64, q=8192, sf=12288)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    rc = mf.lib().moe_ffn_quantize_activations(p(a["x"]), a["T"], a["H"], p(a["q"]), p(a["sf"]), None)
+    assert rc == code
