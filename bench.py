@@ -12,7 +12,8 @@ MFMA peak), plus the T=128 weight-streaming workload (HBM-bound: fraction of
 the 8 TB/s HBM peak) under "secondary", the roofline of the kernel and the
 CPU oracle timed on a bounded token sample.  The pre-dispatch activation
 quantisation (bf16 x of the headline shape -> e4m3 + e8m0) is timed under
-"quantize" (HBM-bound).
+"quantize" (HBM-bound), the gate + top-k router of the same shape under
+"router".
 """
 from __future__ import annotations
 
@@ -165,6 +166,44 @@ def run_quantize(T: int, H: int, steps: int, warmup: int, log):
                                             "per element)"}}
 
 
+def run_router(T: int, H: int, E: int, k: int, steps: int, warmup: int, log):
+    """Gate + top-k (softmax router) on the headline shape; the logits GEMM streams x once."""
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_histogram_amd as mf
+    from mixture_experts_ffn_histogram_amd import synth
+
+    dev = torch.device("cuda:0")
+    x = torch.from_numpy(synth.activations_bf16(T, H, seed=T).view(np.int16)).to(dev)
+    wg = torch.from_numpy(synth.router_weights_bf16(E, H, seed=E).view(np.int16)).to(dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        mf.route_topk(x, wg, logits, idx, w, stream)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(steps):
+        mf.route_topk(x, wg, logits, idx, w, stream)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / steps
+    nbytes = T * H * 2 + E * H * 2 + T * k * 8
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = 2.0 * T * E * H / (ms * 1e-3) / 1e12
+    log(f"[bench] router T={T} H={H} E={E} k={k}: {ms * 1e3:.1f} us/call, {gbs:.0f} GB/s, {tflops:.0f} TFLOP/s")
+    return {"workload": f"router_softmax_top{k}_T{T}_H{H}_E{E}", "us_per_call": round(ms * 1e3, 2),
+            "useful_tflops": round(tflops, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                         "kernel": "router_logits_kernel + router_topk_kernel",
+                         "work_per_launch": f"{nbytes} algorithmic bytes (x, gate weights, top-k outputs)"}}
+
+
 def cpu_baseline(p, clamp: float, target_s: float, log):
     """The CPU oracle as it stands, per-token path, on a bounded token sample."""
     import numpy as np
@@ -201,7 +240,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quantize", action="store_true",
-                    help="skip the pre-dispatch activation quantisation timing")
+                    help="skip the timings of the steps before the forward (quantisation, router)")
     ap.add_argument("--threads", type=int, default=min(16, os.cpu_count() or 8))
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (read + write) a few times, for scaling the "
@@ -269,6 +308,7 @@ def main() -> int:
                          "work_per_launch": f"{sec['bytes']} algorithmic bytes ({sec['active']} active experts)"}}
     if not args.no_quantize:
         out["quantize"] = run_quantize(p["T"], p["H"], args.steps, args.warmup, log)
+        out["router"] = run_router(p["T"], p["H"], p["E"], p["k"], args.steps, args.warmup, log)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(p, main_r["cfg"].clamp, args.cpu_seconds, log)
     print(json.dumps(out), flush=True)

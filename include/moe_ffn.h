@@ -163,6 +163,31 @@ int moe_ffn_transform_weight_scales(const uint8_t* src, uint8_t* dst, int64_t nu
 int moe_ffn_quantize_activations(const void* x_bf16, int64_t num_tokens, int64_t hidden, void* x_e4m3,
                                  uint8_t* x_sf, void* stream);
 
+/* Gate and top-k: the router that produces topk_idx / topk_weights for
+   moe_ffn_forward ("[Blackwell] Reserve SMs for DeepGEMM MegaMoE grid
+   barriers", Fix section: gate computation and top-k selection run before
+   the MegaMoE call).  The pages give no formula; it is a softmax router:
+     logits[t, e] = sum_h x[t, h] * w_gate[e, h]   (bf16 inputs, fp32 sum)
+     topk_idx[t, :] = the top_k experts of largest logit, in descending
+                      order; equal logits: the lower expert id first
+     topk_weights[t, j] = exp(logits[t, idx_j] - max) / sum over the chosen
+                      experts (softmax of the top-k, renormalised to 1), fp32.
+   x_bf16: [num_tokens, hidden] bf16 bit patterns; w_gate_bf16: [num_experts,
+   hidden] bf16; logits: [num_tokens, num_experts] fp32, written (also the
+   scratch the top-k reads); topk_idx: [num_tokens, top_k] int32;
+   topk_weights: [num_tokens, top_k] fp32.  All device pointers; x, w_gate
+   and logits 16-byte aligned, topk_idx / topk_weights 4-byte aligned.
+   hidden must be a positive multiple of 64 and num_experts at most 512,
+   else MOE_FFN_ERR_UNSUPPORTED; 1 <= top_k <= min(64,
+   num_experts), else MOE_FFN_ERR_INVALID_ARG; num_tokens = 0 is a no-op.
+   Inputs must be finite.  Two kernels enqueued on `stream` (a hipStream_t;
+   NULL = default stream); asynchronous, allocates nothing, capturable.
+   MOE_FFN_ERR_INVALID_ARG also for negative sizes and null or misaligned
+   pointers with num_tokens > 0; MOE_FFN_ERR_HIP when a launch fails. */
+int moe_ffn_route_topk(const void* x_bf16, const void* w_gate_bf16, int64_t num_tokens, int64_t hidden,
+                       int64_t num_experts, int64_t top_k, float* logits, int32_t* topk_idx, float* topk_weights,
+                       void* stream);
+
 /* Text of a return or status code (static string). */
 const char* moe_ffn_strerror(int code);
 

@@ -59,7 +59,7 @@ class WorkspaceView(ctypes.Structure):
 
 EXPORTS = ("moe_ffn_get_workspace_size", "moe_ffn_get_token_alignment", "moe_ffn_forward",
            "moe_ffn_strerror", "moe_ffn_launch_size", "moe_ffn_get_workspace_view",
-           "moe_ffn_transform_weight_scales", "moe_ffn_quantize_activations")
+           "moe_ffn_transform_weight_scales", "moe_ffn_quantize_activations", "moe_ffn_route_topk")
 
 _lib = None
 
@@ -89,6 +89,9 @@ def lib():
         L.moe_ffn_transform_weight_scales.restype = ctypes.c_int
         L.moe_ffn_quantize_activations.argtypes = [P, ctypes.c_int64, ctypes.c_int64, P, P, P]
         L.moe_ffn_quantize_activations.restype = ctypes.c_int
+        L.moe_ffn_route_topk.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                         P, P, P, P]
+        L.moe_ffn_route_topk.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -162,6 +165,25 @@ def quantize_activations(x_bf16, x_e4m3, x_sf, stream=None) -> None:
     rc = lib().moe_ffn_quantize_activations(_ptr(x_bf16), T, H, _ptr(x_e4m3), _ptr(x_sf),
                                             ctypes.c_void_p(stream.cuda_stream))
     _check(rc, "moe_ffn_quantize_activations")
+
+
+def route_topk(x_bf16, w_gate_bf16, logits, topk_idx, topk_weights, stream=None) -> None:
+    """Enqueue moe_ffn_route_topk: x [T, H] and w_gate [E, H] bf16 (int16 or bfloat16 device
+    tensors) -> logits fp32 [T, E], topk_idx int32 [T, k], topk_weights fp32 [T, k]."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    T, H = int(x_bf16.shape[0]), int(x_bf16.shape[1])
+    E, k = int(w_gate_bf16.shape[0]), int(topk_idx.shape[1])
+    for a in (x_bf16, w_gate_bf16, logits, topk_idx, topk_weights):
+        assert a.is_contiguous()
+    assert x_bf16.element_size() == 2 and w_gate_bf16.element_size() == 2 and int(w_gate_bf16.shape[1]) == H
+    assert tuple(logits.shape) == (T, E) and logits.dtype == torch.float32
+    assert tuple(topk_idx.shape) == (T, k) and topk_idx.dtype == torch.int32
+    assert tuple(topk_weights.shape) == (T, k) and topk_weights.dtype == torch.float32
+    rc = lib().moe_ffn_route_topk(_ptr(x_bf16), _ptr(w_gate_bf16), T, H, E, k, _ptr(logits), _ptr(topk_idx),
+                                  _ptr(topk_weights), ctypes.c_void_p(stream.cuda_stream))
+    _check(rc, "moe_ffn_route_topk")
 
 
 def kmajor_weight_scales(w1_sf, w2_sf, num_experts: int, hidden: int, intermediate: int, stream=None):

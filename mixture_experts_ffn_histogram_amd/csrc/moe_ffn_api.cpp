@@ -129,6 +129,24 @@ int moe_ffn_quantize_activations(const void* x_bf16, int64_t num_tokens, int64_t
   return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 
+int moe_ffn_route_topk(const void* x_bf16, const void* w_gate_bf16, int64_t num_tokens, int64_t hidden,
+                       int64_t num_experts, int64_t top_k, float* logits, int32_t* topk_idx, float* topk_weights,
+                       void* stream) {
+  if (num_tokens < 0 || hidden <= 0 || num_experts <= 0) return MOE_FFN_ERR_INVALID_ARG;
+  if (hidden % 64 != 0 || num_experts > 512 || hidden > (1 << 20)) return MOE_FFN_ERR_UNSUPPORTED;
+  if (top_k < 1 || top_k > 64 || top_k > num_experts) return MOE_FFN_ERR_INVALID_ARG;
+  if (num_tokens == 0) return MOE_FFN_OK;
+  if (num_tokens > (int64_t(1) << 30)) return MOE_FFN_ERR_UNSUPPORTED;
+  if (!x_bf16 || !w_gate_bf16 || !logits || !topk_idx || !topk_weights) return MOE_FFN_ERR_INVALID_ARG;
+  if (!aligned16(x_bf16) || !aligned16(w_gate_bf16) || !aligned16(logits)) return MOE_FFN_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(topk_idx) & 3u) != 0 || (reinterpret_cast<uintptr_t>(topk_weights) & 3u) != 0)
+    return MOE_FFN_ERR_INVALID_ARG;
+  const hipError_t e = moeffn::launch_router(static_cast<const uint16_t*>(x_bf16), static_cast<const uint16_t*>(w_gate_bf16),
+                                             logits, topk_idx, topk_weights, (int)num_tokens, (int)hidden,
+                                             (int)num_experts, (int)top_k, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
 const char* moe_ffn_strerror(int code) {
   switch (code) {
     case MOE_FFN_OK: return "ok";

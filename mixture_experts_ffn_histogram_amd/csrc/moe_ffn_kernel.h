@@ -64,4 +64,8 @@ int max_block_m(int recipe);
 // bf16 -> e4m3 + e8m0 per 1x32 block over n_elems elements (a multiple of 32).
 hipError_t launch_quantize_act(const uint16_t* x, uint8_t* q, uint8_t* sf, int64_t n_elems, hipStream_t stream);
 
+// Softmax router: logits GEMM (bf16 MFMA) then the per-token top-k and renormalised weights.
+hipError_t launch_router(const uint16_t* x, const uint16_t* wg, float* logits, int32_t* idx, float* wts, int T, int H,
+                         int E, int k, hipStream_t stream);
+
 }  // namespace moeffn

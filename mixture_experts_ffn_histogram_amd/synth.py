@@ -227,6 +227,12 @@ def activations_bf16(T: int, H: int, seed: int) -> np.ndarray:
     return torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
+def router_weights_bf16(E: int, H: int, seed: int) -> np.ndarray:
+    """Router (gate) weights Wg [E, H] as bf16 bit patterns, N(0, 1/H): with N(0, 1)
+    activations the logits are about N(0, 1) (the configs' softmax-top-k routing)."""
+    return _bf16_bits(_rng(seed, 101, E, H), (E, H), 1.0 / math.sqrt(H))
+
+
 def make_problem(cfg: Config, T: int | None = None, threads: int = 8, weights=None) -> dict:
     """All inputs of one forward call as numpy arrays (plus the dims)."""
     T = cfg.T if T is None else T

@@ -72,6 +72,7 @@ def lib():
             ("oracle_ffn_row", ctypes.c_int, [P, P, P, i64, i64, P, P, P, P, P, P, P, P, P, P, d, P]),
             ("oracle_num_threads", ctypes.c_int, []),
             ("oracle_quantize_act", ctypes.c_int, [P, i64, i64, P, P]),
+            ("oracle_route_topk", ctypes.c_int, [P, P, i64, i64, i64, i64, P, P, P]),
         ]:
             fn = getattr(L, name)
             fn.restype = res
@@ -224,6 +225,23 @@ def quantize_act(x_bits: np.ndarray):
     if rc < 0:
         raise RuntimeError(f"oracle_quantize_act failed: {rc}")
     return codes, sf
+
+
+def route_topk(x_bits: np.ndarray, wg_bits: np.ndarray, k: int):
+    """Softmax router: x [T, H] and Wg [E, H] bf16 bit patterns -> (logits float64 [T, E],
+    topk_idx int32 [T, k], topk_weights float32 [T, k])."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    wg = np.ascontiguousarray(wg_bits, dtype=np.uint16)
+    T, H = x.shape
+    E = wg.shape[0]
+    assert wg.shape[1] == H
+    logits = np.zeros((T, E), np.float64)
+    idx = np.zeros((T, k), np.int32)
+    w = np.zeros((T, k), np.float32)
+    rc = lib().oracle_route_topk(_ptr(x), _ptr(wg), int(T), int(H), int(E), int(k), _ptr(logits), _ptr(idx), _ptr(w))
+    if rc < 0:
+        raise RuntimeError(f"oracle_route_topk failed: {rc}")
+    return logits, idx, w
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:

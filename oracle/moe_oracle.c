@@ -583,6 +583,50 @@ int oracle_quantize_act(const uint16_t* x, int64_t T, int64_t H, uint8_t* codes,
     return OR_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Gate and top-k (the step that produces topk_idx / topk_weights before    */
+/* dispatch; the sglang page's Fix section: gate computation and top-k      */
+/* selection run before the MegaMoE call).  The pages give no formula; the  */
+/* reading is a softmax router:                                             */
+/*   logits[t, e] = sum_h x[t, h] * Wg[e, h]   (bf16 inputs, double sum in  */
+/*                                              ascending h; stored fp64)   */
+/*   the k slots of token t are its k largest logits in descending order,   */
+/*   equal logits ordered by the lower expert id (softmax is monotonic, so  */
+/*   this is the top-k of the probabilities);                               */
+/*   weight of slot j = softmax over the selected logits only, i.e. the     */
+/*   top-k probabilities renormalised to sum 1, rounded once to fp32.       */
+/* ------------------------------------------------------------------------ */
+int oracle_route_topk(const uint16_t* x, const uint16_t* wg, int64_t T, int64_t H, int64_t E, int64_t k,
+                      double* logits, int32_t* topk_idx, float* topk_w) {
+    int64_t t;
+    if (T < 0 || H <= 0 || E <= 0 || k <= 0 || k > E || (T > 0 && (!x || !wg || !logits || !topk_idx || !topk_w)))
+        return OR_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (t = 0; t < T; t++) {
+        double* l = logits + t * E;
+        unsigned char* taken = (unsigned char*)calloc((size_t)E, 1);
+        double lmax = 0.0, den = 0.0;
+        int64_t e, h, j;
+        for (e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (h = 0; h < H; h++) acc += oracle_dec_bf16(x[t * H + h]) * oracle_dec_bf16(wg[e * H + h]);
+            l[e] = acc;
+        }
+        for (j = 0; j < k; j++) {
+            int64_t best = -1;
+            for (e = 0; e < E; e++)
+                if (!taken[e] && (best < 0 || l[e] > l[best])) best = e;   /* strict: ties keep the lower id */
+            taken[best] = 1;
+            topk_idx[t * k + j] = (int32_t)best;
+        }
+        lmax = l[topk_idx[t * k]];
+        for (j = 0; j < k; j++) den += exp(l[topk_idx[t * k + j]] - lmax);
+        for (j = 0; j < k; j++) topk_w[t * k + j] = (float)(exp(l[topk_idx[t * k + j]] - lmax) / den);
+        free(taken);
+    }
+    return OR_OK;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

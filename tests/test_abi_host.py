@@ -153,3 +153,25 @@ def test_quantize_activations_argument_checks(kw, code):
     p = lambda v: None if v is None else ctypes.c_void_p(v)
     rc = mf.lib().moe_ffn_quantize_activations(p(a["x"]), a["T"], a["H"], p(a["q"]), p(a["sf"]), None)
     assert rc == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=96), mf.ERR_UNSUPPORTED),          # hidden not a multiple of 64
+    (dict(E=513), mf.ERR_UNSUPPORTED),
+    (dict(E=0), mf.ERR_INVALID_ARG),
+    (dict(k=0), mf.ERR_INVALID_ARG),
+    (dict(k=9), mf.ERR_INVALID_ARG),           # top_k > num_experts
+    (dict(E=128, k=65), mf.ERR_INVALID_ARG),   # top_k > 64
+    (dict(T=-1), mf.ERR_INVALID_ARG),
+    (dict(T=0, x=None, w=None, l=None, i=None, p=None), mf.OK),
+    (dict(l=None), mf.ERR_INVALID_ARG),
+    (dict(x=4104), mf.ERR_INVALID_ARG),        # x not 16-byte aligned
+    (dict(i=4098), mf.ERR_INVALID_ARG),        # topk_idx not 4-byte aligned
+])
+def test_route_topk_argument_checks(kw, code):
+    a = dict(x=4096, w=8192, T=4, H=64, E=8, k=2, l=12288, i=16384, p=20480)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    rc = mf.lib().moe_ffn_route_topk(p(a["x"]), p(a["w"]), a["T"], a["H"], a["E"], a["k"], p(a["l"]), p(a["i"]),
+                                     p(a["p"]), None)
+    assert rc == code
