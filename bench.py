@@ -97,12 +97,14 @@ def run_workload(name: str, steps: int, warmup: int, threads: int, log):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
-    # weight transform, once per set of weights (outside the timed calls)
+    # weight transforms, once per set of weights (outside the timed calls)
     km = mf.kmajor_weight_scales(d["w1_sf"], d["w2_sf"], E, H, I) if p["recipe"] == mf.RECIPE_FP8_FP4 else (None, None)
+    wt = mf.tiled_weights(d["w1"], d["w2"], E, H, I) if p["recipe"] == mf.RECIPE_FP8_FP4 else (None, None)
 
     def call():
         m(num_tokens=T, x=d["x"], x_sf=d["x_sf"], topk_idx=d["topk_idx"], topk_weights=d["topk_weights"],
           w1=d["w1"], w1_sf=d["w1_sf"], w2=d["w2"], w2_sf=d["w2_sf"], w1_sf_kmajor=km[0], w2_sf_kmajor=km[1],
+          w1_tiled=wt[0], w2_tiled=wt[1],
           y=y, y_dtype=mf.Y_BF16,
           activation_clamp=cfg.clamp, status=status, stream=stream)
 

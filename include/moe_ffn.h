@@ -105,6 +105,10 @@ typedef struct {
                                  /* per-stage scale fills then read contiguous rows); without them a */
                                  /* large e2m1 call runs on 64-row tiles.  Both must hold the same   */
                                  /* values as w1_sf / w2_sf.                                          */
+    const void* w1_tiled;        /* optional, e2m1 recipe: w1 as written by moe_ffn_transform_weights */
+    const void* w2_tiled;        /* (rows = 2I, k_bytes = H/2) / (rows = H, k_bytes = I/2); NULL =    */
+                                 /* not given.  The 128-row tiles need both (with the K-major scale   */
+                                 /* copies); they must hold the same weights as w1 / w2.              */
 } moe_ffn_args;
 
 /* Bytes of device workspace one in-flight call needs (buffer-size query of the
@@ -187,6 +191,23 @@ int moe_ffn_quantize_activations(const void* x_bf16, int64_t num_tokens, int64_t
 int moe_ffn_route_topk(const void* x_bf16, const void* w_gate_bf16, int64_t num_tokens, int64_t hidden,
                        int64_t num_experts, int64_t top_k, float* logits, int32_t* topk_idx, float* topk_weights,
                        void* stream);
+
+/* Weight transform for the e2m1 recipe (the weight transform step of the
+   pages' host API, done once per set of weights): re-orders each expert's
+   packed e2m1 weight matrix [rows, k_bytes] into tiles of 16 rows x 64 bytes
+   (one 128-element K stage), each tile 1 KB in MFMA operand order:
+     dst[((e*(rows/16) + b) * (k_bytes/64) + s) * 1024 + (g*16 + r) * 16 + c]
+       = src[(e*rows + 16b + r) * k_bytes + 64s + 16g + c]
+   for r < 16, g < 4, c < 16.  The 128-row tiles then load one contiguous
+   1 KB piece per 16 weight rows and K stage.  For W1 rows = 2I, k_bytes =
+   H/2; for W2 rows = H, k_bytes = I/2.  src and dst: device buffers of
+   num_experts*rows*k_bytes bytes, 16-byte aligned, not overlapping.  Enqueued
+   on `stream` (a hipStream_t; NULL = default stream); asynchronous,
+   allocates nothing.  Returns MOE_FFN_ERR_INVALID_ARG for null or misaligned
+   pointers, non-positive sizes, rows not a multiple of 16 or k_bytes not a
+   multiple of 64, MOE_FFN_ERR_HIP when the launch fails. */
+int moe_ffn_transform_weights(const void* src, void* dst, int64_t num_experts, int64_t rows, int64_t k_bytes,
+                              void* stream);
 
 /* Text of a return or status code (static string). */
 const char* moe_ffn_strerror(int code);

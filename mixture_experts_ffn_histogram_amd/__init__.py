@@ -48,7 +48,8 @@ class Args(ctypes.Structure):
                 ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
                 ("row_to_slot", ctypes.c_void_p), ("slot_to_row", ctypes.c_void_p),
                 ("status", ctypes.c_void_p),
-                ("w1_sf_kmajor", ctypes.c_void_p), ("w2_sf_kmajor", ctypes.c_void_p)]
+                ("w1_sf_kmajor", ctypes.c_void_p), ("w2_sf_kmajor", ctypes.c_void_p),
+                ("w1_tiled", ctypes.c_void_p), ("w2_tiled", ctypes.c_void_p)]
 
 
 class WorkspaceView(ctypes.Structure):
@@ -59,7 +60,8 @@ class WorkspaceView(ctypes.Structure):
 
 EXPORTS = ("moe_ffn_get_workspace_size", "moe_ffn_get_token_alignment", "moe_ffn_forward",
            "moe_ffn_strerror", "moe_ffn_launch_size", "moe_ffn_get_workspace_view",
-           "moe_ffn_transform_weight_scales", "moe_ffn_quantize_activations", "moe_ffn_route_topk")
+           "moe_ffn_transform_weight_scales", "moe_ffn_quantize_activations", "moe_ffn_route_topk",
+           "moe_ffn_transform_weights")
 
 _lib = None
 
@@ -92,6 +94,8 @@ def lib():
         L.moe_ffn_route_topk.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
                                          P, P, P, P]
         L.moe_ffn_route_topk.restype = ctypes.c_int
+        L.moe_ffn_transform_weights.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
+        L.moe_ffn_transform_weights.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -196,11 +200,31 @@ def kmajor_weight_scales(w1_sf, w2_sf, num_experts: int, hidden: int, intermedia
     return a, b
 
 
+def transform_weights(src, dst, num_experts: int, rows: int, k_bytes: int, stream=None) -> None:
+    """Enqueue moe_ffn_transform_weights: tiled copy of packed e2m1 weights (uint8 device tensors)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    rc = lib().moe_ffn_transform_weights(_ptr(src), _ptr(dst), int(num_experts), int(rows), int(k_bytes),
+                                         ctypes.c_void_p(stream.cuda_stream))
+    _check(rc, "moe_ffn_transform_weights")
+
+
+def tiled_weights(w1, w2, num_experts: int, hidden: int, intermediate: int, stream=None):
+    """Tiled copies of the packed e2m1 W1 and W2 (new device tensors), for the 128-row tiles."""
+    import torch
+    a = torch.empty_like(w1)
+    b = torch.empty_like(w2)
+    transform_weights(w1, a, num_experts, 2 * intermediate, hidden // 2, stream)
+    transform_weights(w2, b, num_experts, hidden, intermediate // 2, stream)
+    return a, b
+
+
 def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, topk_weights,
             w1, w1_sf, w2, w2_sf, y, y_dtype: int, activation_clamp: float,
             reserved_cus: int = -1, max_cus: int = 0, expert_counts=None, expert_offsets=None,
             row_to_slot=None, slot_to_row=None, status=None, stream=None, w1_sf_kmajor=None,
-            w2_sf_kmajor=None) -> None:
+            w2_sf_kmajor=None, w1_tiled=None, w2_tiled=None) -> None:
     """Enqueue moe_ffn_forward on `stream` (default: torch's current stream).
 
     All tensors are device tensors laid out as include/moe_ffn.h states; the
@@ -213,7 +237,8 @@ def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, 
     a = Args(int(num_tokens), _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),
              _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf), _ptr(y), int(y_dtype), float(activation_clamp),
              int(reserved_cus), int(max_cus), _ptr(expert_counts), _ptr(expert_offsets),
-             _ptr(row_to_slot), _ptr(slot_to_row), _ptr(status), _ptr(w1_sf_kmajor), _ptr(w2_sf_kmajor))
+             _ptr(row_to_slot), _ptr(slot_to_row), _ptr(status), _ptr(w1_sf_kmajor), _ptr(w2_sf_kmajor),
+             _ptr(w1_tiled), _ptr(w2_tiled))
     rc = lib().moe_ffn_forward(ctypes.byref(problem), ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                ctypes.c_void_p(stream.cuda_stream))

@@ -147,6 +147,16 @@ int moe_ffn_route_topk(const void* x_bf16, const void* w_gate_bf16, int64_t num_
   return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 
+int moe_ffn_transform_weights(const void* src, void* dst, int64_t num_experts, int64_t rows, int64_t k_bytes,
+                              void* stream) {
+  if (!src || !dst || num_experts <= 0 || rows <= 0 || k_bytes <= 0 || rows % 16 != 0 || k_bytes % 64 != 0)
+    return MOE_FFN_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_FFN_ERR_INVALID_ARG;
+  const hipError_t e = moeffn::launch_transform_weights(static_cast<const uint8_t*>(src), static_cast<uint8_t*>(dst),
+                                                        num_experts, rows, k_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
+}
+
 const char* moe_ffn_strerror(int code) {
   switch (code) {
     case MOE_FFN_OK: return "ok";
@@ -175,6 +185,8 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   if (!bf16 && (!a->w1_sf || !a->w2_sf || !aligned16(a->w1_sf) || !aligned16(a->w2_sf))) return MOE_FFN_ERR_INVALID_ARG;
   const bool km = recipe == MOE_FFN_RECIPE_FP8_FP4 && a->w1_sf_kmajor && a->w2_sf_kmajor;
   if (km && (!aligned16(a->w1_sf_kmajor) || !aligned16(a->w2_sf_kmajor))) return MOE_FFN_ERR_INVALID_ARG;
+  const bool tiled = recipe == MOE_FFN_RECIPE_FP8_FP4 && a->w1_tiled && a->w2_tiled;
+  if (tiled && (!aligned16(a->w1_tiled) || !aligned16(a->w2_tiled))) return MOE_FFN_ERR_INVALID_ARG;
   if (T > 0) {
     if (!a->x || !a->topk_idx || !a->topk_weights || !a->y) return MOE_FFN_ERR_INVALID_ARG;
     if (!aligned16(a->x) || !aligned16(a->y) || !aligned16(a->topk_idx) || !aligned16(a->topk_weights))
@@ -215,6 +227,8 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   k.w2_sf = a->w2_sf;
   k.w1_sf_km = km ? a->w1_sf_kmajor : nullptr;
   k.w2_sf_km = km ? a->w2_sf_kmajor : nullptr;
+  k.w1_t = tiled ? static_cast<const uint8_t*>(a->w1_tiled) : nullptr;
+  k.w2_t = tiled ? static_cast<const uint8_t*>(a->w2_tiled) : nullptr;
   k.y = a->y;
   k.out_counts = a->expert_counts;
   k.out_offsets = a->expert_offsets;
@@ -239,7 +253,8 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   const long bm_env = env_long("MOE_FFN_BLOCK_M", 0);  // tuning override: 16, 32, 64 or 128
   if ((bm_env == 16 || bm_env == 32 || bm_env == 64 || bm_env == 128) && bm_env <= moeffn::max_block_m(recipe))
     bm = (int)bm_env;
-  if (bm == 128 && (!big_ok || !km || L.hsg == L.xsg)) bm = 64;  // the 128-row tiles read the K-major weight scales
+  // the 128-row tiles read the K-major weight scales and the tiled weights
+  if (bm == 128 && (!big_ok || !km || !tiled || L.hsg == L.xsg)) bm = 64;
   if (env_long("MOE_FFN_LOG", 0) > 0)
     std::fprintf(stderr, "moe_ffn: T=%lld recipe=%d grid=%d (CUs %d, reserve %d, cap %d) block_m=%d\n",
                  (long long)T, recipe, grid, cus, reserve, a->max_cus, bm);

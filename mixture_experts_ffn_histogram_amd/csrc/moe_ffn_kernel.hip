@@ -847,7 +847,7 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
   auto load_a = [&](int slot, int s) {
     const uint32_t voff = s < nk ? a_off : kBufDead;
 #pragma unroll
-    for (int j = 0; j < 4; j++) ar[slot][j] = buf_load16(rW, voff, a_soff[j] + (uint32_t)s * 64);
+    for (int j = 0; j < 4; j++) ar[slot][j] = buf_load16(rW, voff, a_soff[j] + (uint32_t)s * 1024);
   };
   // Stage s into ring buffer `buf`: 2*NT x 1 KB of routed-row bytes, whole
   // 128-byte lines: instruction q holds rows 8q..8q+7, its lane l row
@@ -955,7 +955,8 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   const int nk = K / 128;
   const uint32_t arow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
   const uint32_t wrows = l1 ? 2u * (uint32_t)I : (uint32_t)H;
-  const uint8_t* W = l1 ? p.w1 + (size_t)e * wrows * arow : p.w2 + (size_t)e * wrows * arow;
+  // the tiled weight copy: 16-row block b, K stage s at (b * nk + s) KB, in MFMA lane order
+  const uint8_t* W = l1 ? p.w1_t + (size_t)e * wrows * arow : p.w2_t + (size_t)e * wrows * arow;
   const uint8_t* Ws = l1 ? p.w1_sf_km + (size_t)e * wrows * srow : p.w2_sf_km + (size_t)e * wrows * srow;
   int rb[4];  // first weight row of each 16-row block of this wave
   if (l1) {
@@ -968,10 +969,13 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   const bool active = l1 || rb[0] < H;
   uint32_t a_soff[4];
 #pragma unroll
-  for (int j = 0; j < 4; j++) a_soff[j] = (uint32_t)rb[j] * arow;
+  for (int j = 0; j < 4; j++) a_soff[j] = (uint32_t)(rb[j] >> 4) * (uint32_t)nk * 1024u;
   const rsrc_t rW = make_rsrc(W, wrows * arow);
   const rsrc_t rWs = make_rsrc(Ws, wrows * srow);
-  const uint32_t a_off = (uint32_t)r16 * arow + (uint32_t)g * 16;
+  // one 1 KB contiguous load per 16-row block and stage: every quad of lanes
+  // reads one 64-byte segment (the texture unit's rate is set by the number
+  // of distinct segments a quad touches; row-strided operand loads touch 4)
+  const uint32_t a_off = (uint32_t)lane * 16u;
   // K-major weight scales: lane l fetches tile rows 4l..4l+3 of the wave's block
   // (L1: gate rows of the tile for l < 32, up rows for l >= 32)
   const uint32_t as_off = l1 ? (uint32_t)((lane < 32 ? 0 : I) + nb * 128 + 4 * (lane & 31))
@@ -1597,6 +1601,29 @@ hipError_t launch_transform_scales(const uint8_t* src, uint8_t* dst, int64_t E, 
   if ((kb + 63) / 64 > 0x7FFFFFFF || (rows + 63) / 64 > 65535 || E > 65535) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((kb + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)E);
   hipLaunchKernelGGL(transform_scales_kernel, grid, dim3(256), 0, stream, src, dst, rows, kb);
+  return hipGetLastError();
+}
+
+// Tiled e2m1 weight copy (one thread per 16-byte chunk of a row).
+__global__ __launch_bounds__(256) void transform_weights_kernel(const uint8_t* __restrict__ src,
+                                                                uint8_t* __restrict__ dst, int64_t E, int64_t rows,
+                                                                int64_t kbytes) {
+  const int64_t cpr = kbytes >> 4;  // 16-byte chunks per row
+  const int64_t n = E * rows * cpr;
+  const int64_t nst = kbytes >> 6;  // 64-byte K stages per row
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n; c += (int64_t)gridDim.x * 256) {
+    const int64_t row = c / cpr, ch = c - row * cpr;  // row over all experts (rows % 16 == 0)
+    const int64_t b = row >> 4, r = row & 15, s = ch >> 2, g = ch & 3;
+    *(v4i*)(dst + ((b * nst + s) << 10) + ((g * 16 + r) << 4)) = ldg16(src + (c << 4));
+  }
+}
+
+hipError_t launch_transform_weights(const uint8_t* src, uint8_t* dst, int64_t E, int64_t rows, int64_t kbytes,
+                                    hipStream_t stream) {
+  const int64_t n = E * rows * (kbytes >> 4);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(transform_weights_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src, dst, E, rows, kbytes);
   return hipGetLastError();
 }
 

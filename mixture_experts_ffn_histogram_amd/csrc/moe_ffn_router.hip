@@ -36,7 +36,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const uin
                                                                        float* __restrict__ logits, int T, int H,
                                                                        int E) {
   __shared__ v4f red[4][8][64];  // K-half 1 partials of each token group: [group][j*2+t][lane]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int tg = wave & 3, kh = wave >> 2;
   const int r16 = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * kRouterTok + tg * 32;
@@ -93,13 +93,21 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const uin
     load(0, step(0));
     load(1, step(1));
     int s = 0;
+    // scheduling barriers keep each step's loads ahead of the MFMAs that do
+    // not need them: a step waits only for its own buffer, two steps old
     for (; s + 3 <= n; s += 3) {
       load(2, step(s + 2));
+      __builtin_amdgcn_sched_barrier(0);
       compute(0);
+      __builtin_amdgcn_sched_barrier(0);
       load(0, step(s + 3));
+      __builtin_amdgcn_sched_barrier(0);
       compute(1);
+      __builtin_amdgcn_sched_barrier(0);
       load(1, step(s + 4));
+      __builtin_amdgcn_sched_barrier(0);
       compute(2);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (s < n) compute(0);
     if (s + 1 < n) compute(1);

@@ -56,10 +56,13 @@ class Runner:
         self.m = mf.MoeFFN(self.max_tokens, p["H"], p["I"], p["E"], p["k"], p["recipe"])
         self.d = upload(p)
         H, E, k = p["H"], p["E"], p["k"]
-        # K-major weight-scale copies (the 128-row tiles need them; other tiles ignore them)
+        # K-major weight-scale copies and tiled weights (the 128-row tiles need them; other tiles
+        # ignore them)
         self.km = (None, None)
+        self.wt = (None, None)
         if kmajor and p["recipe"] == mf.RECIPE_FP8_FP4:
             self.km = mf.kmajor_weight_scales(self.d["w1_sf"], self.d["w2_sf"], E, H, p["I"])
+            self.wt = mf.tiled_weights(self.d["w1"], self.d["w2"], E, H, p["I"])
         self.y = torch.empty((max(self.max_tokens, 1), H), dtype=torch.float32 if self.y_fp32 else torch.int16,
                              device="cuda")
         self.counts = torch.empty(E, dtype=torch.int32, device="cuda")
@@ -84,7 +87,8 @@ class Runner:
                    activation_clamp=self.p["clamp"] if clamp is None else clamp,
                    reserved_cus=reserved_cus, max_cus=max_cus, expert_counts=self.counts,
                    expert_offsets=self.offsets, row_to_slot=self.r2s, slot_to_row=self.s2r,
-                   status=self.status, stream=stream, w1_sf_kmajor=self.km[0], w2_sf_kmajor=self.km[1])
+                   status=self.status, stream=stream, w1_sf_kmajor=self.km[0], w2_sf_kmajor=self.km[1],
+                   w1_tiled=self.wt[0], w2_tiled=self.wt[1])
 
     def y_float(self, T=None) -> np.ndarray:
         T = self.T if T is None else T

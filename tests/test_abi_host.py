@@ -175,3 +175,18 @@ def test_route_topk_argument_checks(kw, code):
     rc = mf.lib().moe_ffn_route_topk(p(a["x"]), p(a["w"]), a["T"], a["H"], a["E"], a["k"], p(a["l"]), p(a["i"]),
                                      p(a["p"]), None)
     assert rc == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(src=None), mf.ERR_INVALID_ARG),
+    (dict(rows=24), mf.ERR_INVALID_ARG),       # rows not a multiple of 16
+    (dict(kb=96), mf.ERR_INVALID_ARG),         # k_bytes not a multiple of 64
+    (dict(E=0), mf.ERR_INVALID_ARG),
+    (dict(dst=8200), mf.ERR_INVALID_ARG),      # dst not 16-byte aligned
+])
+def test_transform_weights_argument_checks(kw, code):
+    a = dict(src=4096, dst=8192, E=2, rows=32, kb=128)
+    a.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    rc = mf.lib().moe_ffn_transform_weights(p(a["src"]), p(a["dst"]), a["E"], a["rows"], a["kb"], None)
+    assert rc == code

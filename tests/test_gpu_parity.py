@@ -247,6 +247,21 @@ def test_transform_weight_scales_bitexact(E, rows, kb):
     assert np.array_equal(d.cpu().numpy(), np.ascontiguousarray(src.transpose(0, 2, 1)))
 
 
+@pytest.mark.parametrize("E,rows,kbytes", [(3, 16, 64), (2, 48, 192), (2, 4096, 3584), (1, 7168, 1024)])
+def test_transform_weights_bitexact(E, rows, kbytes):
+    import mixture_experts_ffn_histogram_amd as mf
+    rng = np.random.default_rng(rows + kbytes)
+    src = rng.integers(0, 256, size=(E, rows, kbytes), dtype=np.uint8)
+    s = torch.from_numpy(src).cuda()
+    d = torch.full((E, rows, kbytes), 0xA5, dtype=torch.uint8, device="cuda")
+    log(f"weight transform E={E} rows={rows} kbytes={kbytes}")
+    mf.transform_weights(s, d, E, rows, kbytes)
+    torch.cuda.synchronize()
+    # [e][b][r][s][g][c] -> [e][b][s][g][r][c]: 16-row blocks, 64-byte stages, lane g*16 + r
+    ref = src.reshape(E, rows // 16, 16, kbytes // 64, 4, 16).transpose(0, 1, 3, 4, 2, 5)
+    assert np.array_equal(d.cpu().numpy().reshape(-1), np.ascontiguousarray(ref).reshape(-1))
+
+
 def test_large_call_without_kmajor_scales_uses_64_row_tiles(monkeypatch):
     # the 128-row tiles need the K-major weight-scale copies; without them the
     # call runs on 64-row tiles and must give the same answer
