@@ -1088,7 +1088,11 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
 #ifndef MOEFFN_W4_PP
 #define MOEFFN_W4_PP 2
 #endif
-template <int BM>
+// TILED: the weights come from the tiled copy (one contiguous 1 KB load per
+// 16-row block and K stage, already in operand order) instead of the
+// row-major matrix (two whole-line loads per block and stage pair, rebuilt by
+// the DPP shuffle).
+template <int BM, bool TILED>
 __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s, bool local, bool l1, int e, int mb,
                              int blk) {
   constexpr int NTB = BM / 16;
@@ -1103,7 +1107,8 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
   const int npairs = (nk + 1) / 2;
   const uint32_t arow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
   const uint32_t wrows = l1 ? 2u * (uint32_t)I : (uint32_t)H;
-  const uint8_t* W = l1 ? p.w1 + (size_t)e * wrows * arow : p.w2 + (size_t)e * wrows * arow;
+  const uint8_t* W = TILED ? (l1 ? p.w1_t : p.w2_t) + (size_t)e * wrows * arow
+                           : (l1 ? p.w1 : p.w2) + (size_t)e * wrows * arow;
   const uint8_t* Ws = l1 ? p.w1_sf + (size_t)e * wrows * srow : p.w2_sf + (size_t)e * wrows * srow;
   int rb[4];
   if (l1) {
@@ -1115,7 +1120,7 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
   }
   const rsrc_t rW = make_rsrc(W, wrows * arow);
   const rsrc_t rWs = make_rsrc(Ws, wrows * srow);
-  const uint32_t a_voff = (uint32_t)(r16 & 7) * arow + (uint32_t)(4 * (r16 >> 3) + g) * 16;
+  const uint32_t a_voff = TILED ? (uint32_t)lane * 16u : (uint32_t)(r16 & 7) * arow + (uint32_t)(4 * (r16 >> 3) + g) * 16;
   const uint32_t as_voff = (uint32_t)r16 * srow;
 
   // routed rows: load half i of token block t covers tile rows t*16 + 8i .. +7
@@ -1170,7 +1175,12 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
 #pragma unroll
     for (int j = 0; j < 4; j++) {
 #pragma unroll
-      for (int i = 0; i < 2; i++) ar[slot][j][i] = buf_load16(rW, a_voff, (uint32_t)(rb[j] + 8 * i) * arow + (uint32_t)m * 128);
+      for (int i = 0; i < 2; i++) {
+        if constexpr (TILED)  // stage 2m + i of 16-row block rb[j] / 16
+          ar[slot][j][i] = buf_load16(rW, a_voff, ((uint32_t)(rb[j] >> 4) * (uint32_t)nk + 2u * (uint32_t)m + i) * 1024u);
+        else
+          ar[slot][j][i] = buf_load16(rW, a_voff, (uint32_t)(rb[j] + 8 * i) * arow + (uint32_t)m * 128);
+      }
       if (slot == 0)
         sga[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rWs, as_voff, (uint32_t)rb[j] * srow + (uint32_t)m * 8, 0));
     }
@@ -1190,7 +1200,8 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
     int sa[4];
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-      a[j] = line_shuffle(ar[slot][j][0], ar[slot][j][1], par, lo);
+      if constexpr (TILED) a[j] = par == 0 ? ar[slot][j][0] : ar[slot][j][1];
+      else a[j] = line_shuffle(ar[slot][j][0], ar[slot][j][1], par, lo);
       const uint32_t sw = slot == 0 ? (par == 0 ? sga[j].x : sga[j].y) : (par == 0 ? nxa[j].x : nxa[j].y);
       sa[j] = (int)(sw >> (8 * g));
     }
@@ -1320,8 +1331,12 @@ __device__ void phase_wave_tiles(const KParams& p, Shared& sh, const int* lr2s, 
     int e, mb, blk;
     decode_tile(sh, E, NB, (int)t, e, mb, blk);
     if constexpr (RECIPE == 2) {
-      wave_tile_w4<BM>(p, sh, lr2s, local, l1, __builtin_amdgcn_readfirstlane(e), __builtin_amdgcn_readfirstlane(mb),
-                       __builtin_amdgcn_readfirstlane(blk));
+      if (p.w1_t)
+        wave_tile_w4<BM, true>(p, sh, lr2s, local, l1, __builtin_amdgcn_readfirstlane(e),
+                               __builtin_amdgcn_readfirstlane(mb), __builtin_amdgcn_readfirstlane(blk));
+      else
+        wave_tile_w4<BM, false>(p, sh, lr2s, local, l1, __builtin_amdgcn_readfirstlane(e),
+                                __builtin_amdgcn_readfirstlane(mb), __builtin_amdgcn_readfirstlane(blk));
     } else {
       wave_tile<RECIPE, BM>(p, sh, lr2s, local, l1, e, mb, blk);
     }
