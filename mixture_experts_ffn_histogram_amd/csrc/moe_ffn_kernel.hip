@@ -851,9 +851,11 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
   };
   // Stage s into ring buffer `buf`: 2*NT x 1 KB of routed-row bytes, whole
   // 128-byte lines: instruction q holds rows 8q..8q+7, its lane l row
-  // 8q + (l%16)/2, 16-byte chunk 4*((l&1)^(q&1)) + l/16 (wave w issues
-  // q = RP*w .. RP*w + RP-1; brd0/brd1 address a lane's MFMA operand bytes
-  // 0-15 / 16-31 of routed-row block 0), the routed-row scale dwords (waves
+  // 8q + l/8 and 16-byte chunk (l%8) ^ f, f = 4*(q&1) + l/16 (half the row's
+  // index in its 16-row block), so every quad of lanes reads one 64-byte
+  // segment and the operand reads below are free of LDS bank conflicts
+  // (wave w issues q = RP*w .. RP*w + RP-1; brd0/brd1 address a lane's MFMA
+  // operand bytes 0-15 / 16-31 of routed-row block 0), the routed-row scale dwords (waves
   // beyond the first copy load zeros from past the end of the buffer into
   // further copies, so every wave issues the same count) and the weight-row
   // scales of the stage from the K-major copy: wave w fetches block 4s+w of
@@ -987,9 +989,9 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   for (int j = 0; j < 4; j++) sa_j[j] = l1 ? (j >> 1) * 128 + (j & 1) * 16 : j * 16;
 
   // routed rows of the tile (rows past the expert repeat its first row / read
-  // padding): fill instruction i of this wave covers rows 8*(RP*wave + i) + (l%16)/2
+  // padding): fill instruction i of this wave covers rows 8*(RP*wave + i) + l/8
   constexpr int RP = big_row_pieces<NT>();
-  const int c8 = r16 >> 1;
+  const int r8 = lane >> 3;
   const int ms = NT == 8 ? (wave & 1) * 64 + lane : lane;
   rsrc_t rX, rXs;
   uint32_t xoff[4] = {0u, 0u, 0u, 0u}, xs_off;
@@ -998,9 +1000,9 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
     rXs = make_rsrc(p.xsg, (uint32_t)(H / 128) * (uint32_t)p.sg_rows * 4u);
 #pragma unroll
     for (int i = 0; i < RP; i++) {
-      const int q = wave * RP + i, m = 8 * q + c8;
+      const int q = wave * RP + i, m = 8 * q + r8;
       const uint32_t tok = (uint32_t)(route_slot(p, nullptr, false, row0 + (m < nrows ? m : 0)) / p.k);
-      xoff[i] = tok * (uint32_t)H + (uint32_t)((((lane & 1) ^ (q & 1)) * 4 + g) * 16);
+      xoff[i] = tok * (uint32_t)H + (uint32_t)(((lane & 7) ^ (4 * (q & 1) + (lane >> 4))) * 16);
     }
     xs_off = (uint32_t)(row0 + ms) * 4u;
   } else {
@@ -1010,12 +1012,12 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
 #pragma unroll
     for (int i = 0; i < RP; i++) {
       const int q = wave * RP + i;
-      xoff[i] = (uint32_t)(row0 + 8 * q + c8) * (uint32_t)I + (uint32_t)((((lane & 1) ^ (q & 1)) * 4 + g) * 16);
+      xoff[i] = (uint32_t)(row0 + 8 * q + r8) * (uint32_t)I + (uint32_t)(((lane & 7) ^ (4 * (q & 1) + (lane >> 4))) * 16);
     }
     xs_off = (uint32_t)(row0 + ms) * 4u;
   }
-  const uint32_t brd0 = (uint32_t)(((r16 >> 3) * 64 + g * 16 + 2 * (r16 & 7) + (0 ^ (r16 >> 3))) * 16);
-  const uint32_t brd1 = (uint32_t)(((r16 >> 3) * 64 + g * 16 + 2 * (r16 & 7) + (1 ^ (r16 >> 3))) * 16);
+  const uint32_t brd0 = (uint32_t)(((r16 >> 3) * 64 + (r16 & 7) * 8 + (g ^ (r16 >> 1))) * 16);
+  const uint32_t brd1 = (uint32_t)(((r16 >> 3) * 64 + (r16 & 7) * 8 + ((4 + g) ^ (r16 >> 1))) * 16);
   // A wave whose scale dwords would repeat rows another wave already loads
   // reads past the end of the buffer instead: that load returns zeros without
   // a memory access (each dword it would fetch is a cache line of its own),
