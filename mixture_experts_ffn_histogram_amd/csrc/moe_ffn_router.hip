@@ -14,7 +14,7 @@
 // order through LDS, so the result is deterministic).  The gate rows are the
 // A operand, so a lane holds 4 consecutive experts of one token and stores
 // them as one 16-byte piece of the logits row.  Both operands are read
-// K-contiguous, 32 bytes per lane per 64-element K step, two steps ahead.  router_topk_kernel: one wave per
+// K-contiguous, 64 bytes per quad of lanes, two 64-element K steps ahead.  router_topk_kernel: one wave per
 // token, k rounds of a wave-wide (value desc, id asc) maximum, then the
 // renormalised softmax of the chosen logits in fp32.
 #include <hip/hip_runtime.h>
@@ -43,15 +43,22 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const uin
   const int e0 = blockIdx.y * kRouterExp;
   const int nblk = min(4, (E - e0 + 15) / 16);  // 16-expert blocks holding an expert < E
 
-  // lane (r16, g): A row = expert e0 + 16j + r16, B row = token t0 + 16t + r16
-  // (rows past the end read the last row; their results are not stored);
-  // K elements g*16 .. g*16+15 of each 64-element step (MFMA h takes 8 of them)
+  // Loads read one 64-byte segment per quad of lanes (the texture unit
+  // spends a cycle per distinct segment a quad touches): load h of a 16-row
+  // block gives lane 16G + 4A + U row 4A + G, 16-byte chunk 4h + U.  A 4x4
+  // lane transpose (ds_bpermute, swapping lane bits 0-1 with 4-5) then puts
+  // row r, chunk 4h + g in lane (r, g): MFMA h's operand, K elements
+  // 32h + 8g .. +7, the same order for A and B.  Rows past the end read the
+  // last row; their results are not stored.
+  const int rq = (lane & 12) | (lane >> 4);                   // row of the block this lane loads
+  const int cq = (lane & 3) * 8;                              // its element offset in a 32-element half
+  const int src = (((lane & 3) << 4) | (lane & 12) | (lane >> 4)) * 4;
   const uint16_t* ap[4];
   const uint16_t* bp[2];
 #pragma unroll
-  for (int j = 0; j < 4; j++) ap[j] = wg + (size_t)min(e0 + 16 * j + r16, E - 1) * H + g * 16;
+  for (int j = 0; j < 4; j++) ap[j] = wg + (size_t)min(e0 + 16 * j + rq, E - 1) * H + cq;
 #pragma unroll
-  for (int t = 0; t < 2; t++) bp[t] = x + (size_t)min(t0 + 16 * t + r16, T - 1) * H + g * 16;
+  for (int t = 0; t < 2; t++) bp[t] = x + (size_t)min(t0 + 16 * t + rq, T - 1) * H + cq;
 
   v4f acc[4][2];
 #pragma unroll
@@ -64,24 +71,35 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const uin
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       a[buf][j][0] = ldg16(ap[j] + k0);
-      a[buf][j][1] = ldg16(ap[j] + k0 + 8);
+      a[buf][j][1] = ldg16(ap[j] + k0 + 32);
     }
 #pragma unroll
     for (int t = 0; t < 2; t++) {
       b[buf][t][0] = ldg16(bp[t] + k0);
-      b[buf][t][1] = ldg16(bp[t] + k0 + 8);
+      b[buf][t][1] = ldg16(bp[t] + k0 + 32);
     }
+  };
+  auto tr = [&](const v4i& v) {
+    v4i r;
+#pragma unroll
+    for (int c = 0; c < 4; c++) r[c] = __builtin_amdgcn_ds_bpermute(src, v[c]);
+    return r;
   };
   auto compute = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; h++)
+    for (int h = 0; h < 2; h++) {
+      v4i bo[2];
 #pragma unroll
-      for (int j = 0; j < 4; j++)
+      for (int t = 0; t < 2; t++) bo[t] = tr(b[buf][t][h]);
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const v4i ao = tr(a[buf][j][h]);
 #pragma unroll
         for (int t = 0; t < 2; t++)
-          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_r, a[buf][j][h]),
-                                                              __builtin_bit_cast(v8bf_r, b[buf][t][h]), acc[j][t],
-                                                              0, 0, 0);
+          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_r, ao),
+                                                              __builtin_bit_cast(v8bf_r, bo[t]), acc[j][t], 0, 0, 0);
+      }
+    }
   };
   // this wave's half of the K steps, two steps in flight ahead of the one in
   // use; loads past the half re-read its last step (never used), so the
