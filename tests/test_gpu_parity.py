@@ -79,13 +79,16 @@ def test_fp8xfp8_config_full():
     log(f"  near-tie code flips in sampled rows: {flips}")
 
 
-@pytest.mark.parametrize("T,E,k", [(96, 32, 8), (40, 8, 4), (333, 8, 3), (1000, 4, 2), (2048, 8, 4)])
-def test_fp8xfp4_reduced_full(T, E, k):
-    # spans token-block sizes 16..128 (average rows per expert 24 .. 1024) and ragged tails
+@pytest.mark.parametrize("T,E,k,prepared", [(64, 32, 8, True), (96, 32, 8, True), (40, 8, 4, True),
+                                             (333, 8, 3, True), (1000, 4, 2, True), (2048, 8, 4, True),
+                                             (64, 32, 8, False), (96, 32, 8, False), (333, 8, 3, False)])
+def test_fp8xfp4_reduced_full(T, E, k, prepared):
+    # spans token-block sizes 16..128 (average rows per expert 16 .. 1024) and ragged tails;
+    # prepared=False: no tiled weights / K-major scales (row-major loads in every tile kind)
     cfg = _small_cfg(synth.RECIPE_FP8_FP4, T, 1024, 512, E, k, "softmax", seed=T + E)
     p = synth.make_problem(cfg, threads=8)
-    log(f"fp8xfp4 reduced T={T} E={E} k={k}")
-    run = Runner(p)
+    log(f"fp8xfp4 reduced T={T} E={E} k={k} prepared={prepared}")
+    run = Runner(p, kmajor=prepared)
     run.run()
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
