@@ -181,8 +181,9 @@ int moe_ffn_quantize_activations(const void* x_bf16, int64_t num_tokens, int64_t
    scratch the top-k reads); topk_idx: [num_tokens, top_k] int32;
    topk_weights: [num_tokens, top_k] fp32.  All device pointers; x, w_gate
    and logits 16-byte aligned, topk_idx / topk_weights 4-byte aligned.
-   hidden must be a positive multiple of 64 and num_experts at most 512,
-   else MOE_FFN_ERR_UNSUPPORTED; 1 <= top_k <= min(64,
+   hidden must be a positive multiple of 64, num_experts at most 512 and
+   num_tokens * hidden * 2 below 2^31, else MOE_FFN_ERR_UNSUPPORTED;
+   1 <= top_k <= min(64,
    num_experts), else MOE_FFN_ERR_INVALID_ARG; num_tokens = 0 is a no-op.
    Inputs must be finite.  Two kernels enqueued on `stream` (a hipStream_t;
    NULL = default stream); asynchronous, allocates nothing, capturable.

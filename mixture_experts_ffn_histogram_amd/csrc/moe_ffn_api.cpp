@@ -136,7 +136,9 @@ int moe_ffn_route_topk(const void* x_bf16, const void* w_gate_bf16, int64_t num_
   if (hidden % 64 != 0 || num_experts > 512 || hidden > (1 << 20)) return MOE_FFN_ERR_UNSUPPORTED;
   if (top_k < 1 || top_k > 64 || top_k > num_experts) return MOE_FFN_ERR_INVALID_ARG;
   if (num_tokens == 0) return MOE_FFN_OK;
-  if (num_tokens > (int64_t(1) << 30)) return MOE_FFN_ERR_UNSUPPORTED;
+  // 32-bit buffer offsets into x and the gate weights
+  if (num_tokens * hidden * 2 >= (int64_t(1) << 31) || num_experts * hidden * 2 >= (int64_t(1) << 31))
+    return MOE_FFN_ERR_UNSUPPORTED;
   if (!x_bf16 || !w_gate_bf16 || !logits || !topk_idx || !topk_weights) return MOE_FFN_ERR_INVALID_ARG;
   if (!aligned16(x_bf16) || !aligned16(w_gate_bf16) || !aligned16(logits)) return MOE_FFN_ERR_INVALID_ARG;
   if ((reinterpret_cast<uintptr_t>(topk_idx) & 3u) != 0 || (reinterpret_cast<uintptr_t>(topk_weights) & 3u) != 0)

@@ -9,14 +9,12 @@
 //
 // Two kernels.  router_logits_kernel: a dense bf16 GEMM on
 // v_mfma_f32_16x16x32_bf16; a workgroup computes 128 tokens x 64 experts
-// with 8 waves (4 groups of 32 tokens x 2 halves of K, all sharing the 64
-// gate rows through the vector L1; the two K halves are added in a fixed
-// order through LDS, so the result is deterministic).  The gate rows are the
-// A operand, so a lane holds 4 consecutive experts of one token and stores
-// them as one 16-byte piece of the logits row.  Both operands are read
-// K-contiguous, 64 bytes per quad of lanes, two 64-element K steps ahead.  router_topk_kernel: one wave per
-// token, k rounds of a wave-wide (value desc, id asc) maximum, then the
-// renormalised softmax of the chosen logits in fp32.
+// (4 waves x 32 tokens); both operands are staged through LDS (see below).
+// The gate rows are the A operand, so a lane holds 4 consecutive experts of
+// one token and stores them as one 16-byte piece of the logits row.
+// router_topk_kernel: one wave per token, k rounds of a wave-wide (value
+// desc, id asc) maximum, then the renormalised softmax of the chosen logits
+// in fp32.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -27,73 +25,69 @@ namespace moeffn {
 
 typedef __bf16 v8bf_r __attribute__((ext_vector_type(8)));
 
-constexpr int kRouterTok = 128;   // tokens per workgroup (4 token groups x 32)
-constexpr int kRouterExp = 64;    // experts per workgroup (4 blocks of 16)
-constexpr int kRouterThreads = 512;  // 8 waves: 4 token groups x 2 halves of K
+constexpr int kRouterTok = 128;                               // tokens per workgroup (4 waves x 32)
+constexpr int kRouterExp = 64;                               // experts per workgroup (4 blocks of 16)
+constexpr int kRouterStage = (kRouterExp + kRouterTok) * 128;  // one 64-element K step: 24 KB
 
-__global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const uint16_t* __restrict__ x,
-                                                                       const uint16_t* __restrict__ wg,
-                                                                       float* __restrict__ logits, int T, int H,
-                                                                       int E) {
-  __shared__ v4f red[4][8][64];  // K-half 1 partials of each token group: [group][j*2+t][lane]
+// Logits tile: 64 gate rows x 128 token rows, both staged through a 3-buffer
+// LDS ring by buffer loads that write LDS directly (fill instruction q holds
+// rows 8q..8q+7 of the stage: q < 8 gate rows, q >= 8 token rows; lane l
+// reads row 8q + l/8, 16-byte chunk (l%8) ^ f, f = 4(q&1) + l/16, so each
+// quad of lanes reads one 64-byte segment and the operand reads are free of
+// LDS bank conflicts), two K steps ahead, one workgroup barrier per step.
+// The waits are explicit (vmcnt before the barrier, issue order pinned by
+// scheduling barriers) and each ring buffer is its own LDS object.
+__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+                                                            const uint16_t* __restrict__ wg,
+                                                            float* __restrict__ logits, int T, int H, int E) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kRouterStage];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[kRouterStage];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[kRouterStage];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int tg = wave & 3, kh = wave >> 2;
   const int r16 = lane & 15, g = lane >> 4;
-  const int t0 = blockIdx.x * kRouterTok + tg * 32;
+  const int t0 = blockIdx.x * kRouterTok;
   const int e0 = blockIdx.y * kRouterExp;
   const int nblk = min(4, (E - e0 + 15) / 16);  // 16-expert blocks holding an expert < E
+  const int nks = H / 64;
 
-  // Loads read one 64-byte segment per quad of lanes (the texture unit
-  // spends a cycle per distinct segment a quad touches): load h of a 16-row
-  // block gives lane 16G + 4A + U row 4A + G, 16-byte chunk 4h + U.  A 4x4
-  // lane transpose (ds_bpermute, swapping lane bits 0-1 with 4-5) then puts
-  // row r, chunk 4h + g in lane (r, g): MFMA h's operand, K elements
-  // 32h + 8g .. +7, the same order for A and B.  Rows past the end read the
-  // last row; their results are not stored.
-  const int rq = (lane & 12) | (lane >> 4);                   // row of the block this lane loads
-  const int cq = (lane & 3) * 8;                              // its element offset in a 32-element half
-  const int src = (((lane & 3) << 4) | (lane & 12) | (lane >> 4)) * 4;
-  const uint16_t* ap[4];
-  const uint16_t* bp[2];
+  // fills of this wave: instructions q = 6 * wave + i (rows past the end read the last row)
+  const rsrc_t rA = make_rsrc(wg, (uint32_t)E * (uint32_t)H * 2u);
+  const rsrc_t rB = make_rsrc(x, (uint32_t)T * (uint32_t)H * 2u);
+  uint32_t voff[6];
 #pragma unroll
-  for (int j = 0; j < 4; j++) ap[j] = wg + (size_t)min(e0 + 16 * j + rq, E - 1) * H + cq;
+  for (int i = 0; i < 6; i++) {
+    const int q = 6 * wave + i;
+    const int rr = (q < 8 ? 8 * q : 8 * (q - 8)) + (lane >> 3);
+    const int row = q < 8 ? min(e0 + rr, E - 1) : min(t0 + rr, T - 1);
+    voff[i] = (uint32_t)row * (uint32_t)H * 2u + (uint32_t)(((lane & 7) ^ (4 * (q & 1) + (lane >> 4))) * 16);
+  }
+  auto dma = [&](int s, uint8_t* buf) {
 #pragma unroll
-  for (int t = 0; t < 2; t++) bp[t] = x + (size_t)min(t0 + 16 * t + rq, T - 1) * H + cq;
+    for (int i = 0; i < 6; i++) {
+      const int q = 6 * wave + i;
+      buf_load_lds16(q < 8 ? rA : rB, buf + q * 1024, s < nks ? voff[i] : kBufDead, (uint32_t)s * 128u);
+    }
+  };
+  // operand of MFMA h for 16-row block b of a region: row r16, chunk 4h + g
+  const uint32_t rd0 = (uint32_t)((r16 >> 3) * 1024 + (r16 & 7) * 128);
+  uint32_t rdc[2];
+#pragma unroll
+  for (int h = 0; h < 2; h++) rdc[h] = rd0 + (uint32_t)((((4 * h + g) ^ (r16 >> 1))) * 16);
 
   v4f acc[4][2];
 #pragma unroll
   for (int j = 0; j < 4; j++)
 #pragma unroll
     for (int t = 0; t < 2; t++) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
-  v4i a[3][4][2], b[3][2][2];
-  auto load = [&](int buf, int ks) {
-    const size_t k0 = (size_t)ks * 64;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-      a[buf][j][0] = ldg16(ap[j] + k0);
-      a[buf][j][1] = ldg16(ap[j] + k0 + 32);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; t++) {
-      b[buf][t][0] = ldg16(bp[t] + k0);
-      b[buf][t][1] = ldg16(bp[t] + k0 + 32);
-    }
-  };
-  auto tr = [&](const v4i& v) {
-    v4i r;
-#pragma unroll
-    for (int c = 0; c < 4; c++) r[c] = __builtin_amdgcn_ds_bpermute(src, v[c]);
-    return r;
-  };
-  auto compute = [&](int buf) {
+  auto compute = [&](const uint8_t* buf) {
 #pragma unroll
     for (int h = 0; h < 2; h++) {
       v4i bo[2];
 #pragma unroll
-      for (int t = 0; t < 2; t++) bo[t] = tr(b[buf][t][h]);
+      for (int t = 0; t < 2; t++) bo[t] = *(const v4i*)(buf + 8 * 1024 + (2 * wave + t) * 2048 + rdc[h]);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const v4i ao = tr(a[buf][j][h]);
+        const v4i ao = *(const v4i*)(buf + j * 2048 + rdc[h]);
 #pragma unroll
         for (int t = 0; t < 2; t++)
           acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_r, ao),
@@ -101,63 +95,61 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const uin
       }
     }
   };
-  // this wave's half of the K steps, two steps in flight ahead of the one in
-  // use; loads past the half re-read its last step (never used), so the
-  // steady loop carries no branch
-  const int nks = H / 64;
-  const int kb = (nks * kh) / 2, n = (nks * (kh + 1)) / 2 - kb;
-  if (n > 0) {
-    auto step = [&](int s) { return kb + min(s, n - 1); };
-    load(0, step(0));
-    load(1, step(1));
-    int s = 0;
-    // scheduling barriers keep each step's loads ahead of the MFMAs that do
-    // not need them: a step waits only for its own buffer, two steps old
-    for (; s + 3 <= n; s += 3) {
-      load(2, step(s + 2));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(0);
-      __builtin_amdgcn_sched_barrier(0);
-      load(0, step(s + 3));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(1);
-      __builtin_amdgcn_sched_barrier(0);
-      load(1, step(s + 4));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (s < n) compute(0);
-    if (s + 1 < n) compute(1);
-  }
 
-  // logits = K-half 0 + K-half 1, in this order
-  if (kh == 1) {
-#pragma unroll
-    for (int j = 0; j < 4; j++)
-#pragma unroll
-      for (int t = 0; t < 2; t++) red[tg][j * 2 + t][lane] = acc[j][t];
+  dma(0, ring0);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(1, ring1);
+  __builtin_amdgcn_sched_barrier(0);
+  int s0 = 0;
+  for (; s0 + 3 <= nks; s0 += 3) {
+    MOEFFN_WAIT_VMCNT(6);  // this wave's fill of step s0 has landed (step s0+1's 6 fills may be in flight)
+    __builtin_amdgcn_s_barrier();
+    dma(s0 + 2, ring2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ring0);
+    __builtin_amdgcn_sched_barrier(0);
+    MOEFFN_WAIT_VMCNT(6);
+    __builtin_amdgcn_s_barrier();
+    dma(s0 + 3, ring0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ring1);
+    __builtin_amdgcn_sched_barrier(0);
+    MOEFFN_WAIT_VMCNT(6);
+    __builtin_amdgcn_s_barrier();
+    dma(s0 + 4, ring1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(ring2);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __syncthreads();
-  if (kh == 1 || t0 >= T) return;
-  // lane (c = r16, g) holds experts e0 + 16j + 4g .. +3 of token t0 + 16t + c
+  // nks % 3 trailing steps, already in flight in ring0 / ring1
+  if (s0 < nks) {
+    MOEFFN_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    compute(ring0);
+  }
+  if (s0 + 1 < nks) {
+    MOEFFN_WAIT_VMCNT(0);
+    __builtin_amdgcn_s_barrier();
+    compute(ring1);
+  }
+  MOEFFN_WAIT_VMCNT(0);  // no fill outlives the workgroup
+
+  // lane (c = r16, g) holds experts e0 + 16j + 4g .. +3 of token t0 + 32 wave + 16t + c
 #pragma unroll
   for (int t = 0; t < 2; t++) {
-    const int tok = t0 + 16 * t + r16;
+    const int tok = t0 + 32 * wave + 16 * t + r16;
     if (tok >= T) continue;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       if (j >= nblk) continue;
-      const v4f o = red[tg][j * 2 + t][lane];
-      const v4f v = v4f{acc[j][t][0] + o[0], acc[j][t][1] + o[1], acc[j][t][2] + o[2], acc[j][t][3] + o[3]};
       const int e = e0 + 16 * j + 4 * g;
       float* dst = logits + (size_t)tok * E + e;
       if ((E & 3) == 0 && e + 4 <= E) {
-        stg16f(dst, v);
+        stg16f(dst, acc[j][t]);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; i++)
-          if (e + i < E) dst[i] = v[i];
+          if (e + i < E) dst[i] = acc[j][t][i];
       }
     }
   }
@@ -220,7 +212,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 hipError_t launch_router(const uint16_t* x, const uint16_t* wg, float* logits, int32_t* idx, float* wts, int T, int H,
                          int E, int k, hipStream_t stream) {
   const dim3 g1((unsigned)((T + kRouterTok - 1) / kRouterTok), (unsigned)((E + kRouterExp - 1) / kRouterExp));
-  hipLaunchKernelGGL(router_logits_kernel, g1, dim3(kRouterThreads), 0, stream, x, wg, logits, T, H, E);
+  hipLaunchKernelGGL(router_logits_kernel, g1, dim3(256), 0, stream, x, wg, logits, T, H, E);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int blocks = (T + 3) / 4;
