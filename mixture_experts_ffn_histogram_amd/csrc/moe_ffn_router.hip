@@ -12,9 +12,9 @@
 // (4 waves x 32 tokens); both operands are staged through LDS (see below).
 // The gate rows are the A operand, so a lane holds 4 consecutive experts of
 // one token and stores them as one 16-byte piece of the logits row.
-// router_topk_kernel: one wave per token, k rounds of a wave-wide (value
-// desc, id asc) maximum, then the renormalised softmax of the chosen logits
-// in fp32.
+// router_topk_kernel: 16 lanes per token, k rounds of a (value desc, id
+// asc) maximum over the row, then the renormalised softmax of the chosen
+// logits in fp32.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -155,56 +155,103 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
 }
 
-constexpr int kTopkMaxPerLane = 8;  // E <= 512
+// Order-preserving integer key of an fp32 logit (a larger float gives a
+// larger signed key; -inf maps above INT32_MIN, which marks "not a candidate").
+// Adding +0 turns -0 into +0, so the two zeros compare equal as they do in fp32.
+__device__ __forceinline__ int topk_key(float f) {
+  const int b = __float_as_int(f + 0.0f);
+  return b >= 0 ? b : b ^ 0x7FFFFFFF;
+}
+__device__ __forceinline__ float topk_val(int key) { return __int_as_float(key >= 0 ? key : key ^ 0x7FFFFFFF); }
 
+// (key desc, id asc) maximum of a lane and its DPP partner.  CTRL: quad_perm
+// [1,0,3,2] (0xB1), quad_perm [2,3,0,1] (0x4E), row_half_mirror (0x141),
+// row_mirror (0x140).
+template <int CTRL>
+__device__ __forceinline__ void topk_merge(int& bk, int& be) {
+  const int ok = __builtin_amdgcn_mov_dpp(bk, CTRL, 0xF, 0xF, false);
+  const int oe = __builtin_amdgcn_mov_dpp(be, CTRL, 0xF, 0xF, false);
+  const bool take = (ok > bk) | ((ok == bk) & (oe < be));
+  bk = take ? ok : bk;
+  be = take ? oe : be;
+}
+
+// Sum over the 16 lanes of a row (the same butterfly in every lane, so every
+// lane ends with the same bits).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+// Top-k: 16 lanes per token (4 tokens per wave).  Lane r holds the keys of
+// experts r, r + 16, ... (NPL of them, E <= 16 * NPL); each of the k rounds
+// takes the lane-local best and reduces it over the 16-lane row with DPP
+// moves (quad swaps, then the half-row and row mirrors), comparing (logit
+// desc, id asc), so equal logits give the lower expert id and the order does
+// not depend on the schedule.  The winner's key is then retired to INT32_MIN.
+// Selects only, no branches, in the k rounds.
+template <int NPL>
 __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits, int32_t* __restrict__ idx,
                                                           float* __restrict__ wts, int T, int E, int k) {
-  const int lane = threadIdx.x & 63;
+  constexpr int kNone = INT32_MIN;
+  const int lane = threadIdx.x & 63, r = lane & 15;
   const int nw = gridDim.x * 4;
-  for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += nw) {
-    float v[kTopkMaxPerLane];
+  for (int tb = blockIdx.x * 4 + (threadIdx.x >> 6); tb * 4 < T; tb += nw) {
+    const int t = tb * 4 + (lane >> 4);
+    const bool tok = t < T;
+    const float* row = logits + (size_t)(tok ? t : T - 1) * E;  // clamped: every load in bounds, no branches
+    int key[NPL];
 #pragma unroll
-    for (int q = 0; q < kTopkMaxPerLane; q++) {
-      const int e = lane + 64 * q;
-      v[q] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+    for (int q = 0; q < NPL; q++) {
+      const int e = r + 16 * q;
+      const float x = row[e < E ? e : E - 1];
+      key[q] = e < E ? topk_key(tok ? x : 0.f) : kNone;
     }
-    uint32_t taken = 0;
-    int my_e = 0;
-    float my_v = -INFINITY, vmax = 0.f;
+    int my_e[4] = {0, 0, 0, 0};
+    int my_k[4] = {kNone, kNone, kNone, kNone};
+    int kmax = 0;
     for (int j = 0; j < k; j++) {
-      float bv = -INFINITY;
-      int be = 0x7FFFFFFF;
+      int bk = kNone, be = 0x7FFFFFFF;
 #pragma unroll
-      for (int q = 0; q < kTopkMaxPerLane; q++) {
-        const int e = lane + 64 * q;
-        if (e < E && !((taken >> q) & 1u) && (v[q] > bv || (v[q] == bv && e < be))) {
-          bv = v[q];
-          be = e;
-        }
+      for (int q = 0; q < NPL; q++) {
+        const bool take = key[q] > bk;  // q ascending: an equal key keeps the lower id
+        bk = take ? key[q] : bk;
+        be = take ? r + 16 * q : be;
       }
+      topk_merge<0xB1>(bk, be);
+      topk_merge<0x4E>(bk, be);
+      topk_merge<0x141>(bk, be);
+      topk_merge<0x140>(bk, be);
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, 64);
-        const int oe = __shfl_xor(be, off, 64);
-        if (ov > bv || (ov == bv && oe < be)) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if ((be & 63) == lane) taken |= 1u << (be >> 6);
-      if (j == 0) vmax = bv;
-      if (lane == j) {
-        my_e = be;
-        my_v = bv;
+      for (int q = 0; q < NPL; q++) key[q] = (be == r + 16 * q) ? kNone : key[q];
+      kmax = j == 0 ? bk : kmax;
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const bool mine = j == 16 * u + r;
+        my_e[u] = mine ? be : my_e[u];
+        my_k[u] = mine ? bk : my_k[u];
       }
     }
-    const float ex = lane < k ? expf(my_v - vmax) : 0.f;
-    float den = ex;
+    const float vmax = topk_val(kmax);
+    float ex[4], part = 0.f;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) den += __shfl_xor(den, off, 64);
-    if (lane < k) {
-      idx[(size_t)t * k + lane] = my_e;
-      wts[(size_t)t * k + lane] = ex / den;
+    for (int u = 0; u < 4; u++) {
+      ex[u] = (16 * u + r < k) ? expf(topk_val(my_k[u]) - vmax) : 0.f;
+      part += ex[u];
+    }
+    const float den = row16_sum(part);
+    if (tok) {
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int jj = 16 * u + r;
+        if (jj < k) {
+          idx[(size_t)t * k + jj] = my_e[u];
+          wts[(size_t)t * k + jj] = ex[u] / den;
+        }
+      }
     }
   }
 }
@@ -215,9 +262,12 @@ hipError_t launch_router(const uint16_t* x, const uint16_t* wg, float* logits, i
   hipLaunchKernelGGL(router_logits_kernel, g1, dim3(256), 0, stream, x, wg, logits, T, H, E);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int blocks = (T + 3) / 4;
+  int blocks = (T + 15) / 16;  // 16 tokens per workgroup
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, logits, idx, wts, T, E, k);
+  if (E <= 256)
+    hipLaunchKernelGGL(router_topk_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, logits, idx, wts, T, E, k);
+  else
+    hipLaunchKernelGGL(router_topk_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, logits, idx, wts, T, E, k);
   return hipGetLastError();
 }
 
