@@ -9,7 +9,8 @@
 //
 // Two kernels.  router_logits_kernel: a dense bf16 GEMM on
 // v_mfma_f32_16x16x32_bf16; a workgroup computes 128 tokens x 64 experts
-// (4 waves x 32 tokens); both operands are staged through LDS (see below).
+// (8 waves x 16 tokens, two waves per SIMD so one hides the other's waits);
+// both operands are staged through LDS (see below).
 // The gate rows are the A operand, so a lane holds 4 consecutive experts of
 // one token and stores them as one 16-byte piece of the logits row.
 // router_topk_kernel: 16 lanes per token, k rounds of a (value desc, id
@@ -25,9 +26,14 @@ namespace moeffn {
 
 typedef __bf16 v8bf_r __attribute__((ext_vector_type(8)));
 
-constexpr int kRouterTok = 128;                               // tokens per workgroup (4 waves x 32)
+constexpr int kRouterTok = 128;                               // tokens per workgroup
 constexpr int kRouterExp = 64;                               // experts per workgroup (4 blocks of 16)
+constexpr int kRouterWaves = 8;                              // 16 tokens per wave
+constexpr int kRouterThreads = 64 * kRouterWaves;
 constexpr int kRouterStage = (kRouterExp + kRouterTok) * 128;  // one 64-element K step: 24 KB
+constexpr int kRouterFills = (kRouterExp + kRouterTok) / 8 / kRouterWaves;  // 8-row fill instructions per wave
+static_assert(kRouterFills * kRouterWaves * 8 == kRouterExp + kRouterTok && kRouterTok == 16 * kRouterWaves,
+              "fills and token blocks must divide evenly over the waves");
 
 // Logits tile: 64 gate rows x 128 token rows, both staged through a 3-buffer
 // LDS ring by buffer loads that write LDS directly (fill instruction q holds
@@ -37,7 +43,7 @@ constexpr int kRouterStage = (kRouterExp + kRouterTok) * 128;  // one 64-element
 // LDS bank conflicts), two K steps ahead, one workgroup barrier per step.
 // The waits are explicit (vmcnt before the barrier, issue order pinned by
 // scheduling barriers) and each ring buffer is its own LDS object.
-__global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const uint16_t* __restrict__ x,
                                                             const uint16_t* __restrict__ wg,
                                                             float* __restrict__ logits, int T, int H, int E) {
   __shared__ __attribute__((aligned(16))) uint8_t ring0[kRouterStage];
@@ -50,21 +56,21 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   const int nblk = min(4, (E - e0 + 15) / 16);  // 16-expert blocks holding an expert < E
   const int nks = H / 64;
 
-  // fills of this wave: instructions q = 6 * wave + i (rows past the end read the last row)
+  // fills of this wave: instructions q = kRouterFills * wave + i (rows past the end read the last row)
   const rsrc_t rA = make_rsrc(wg, (uint32_t)E * (uint32_t)H * 2u);
   const rsrc_t rB = make_rsrc(x, (uint32_t)T * (uint32_t)H * 2u);
-  uint32_t voff[6];
+  uint32_t voff[kRouterFills];
 #pragma unroll
-  for (int i = 0; i < 6; i++) {
-    const int q = 6 * wave + i;
+  for (int i = 0; i < kRouterFills; i++) {
+    const int q = kRouterFills * wave + i;
     const int rr = (q < 8 ? 8 * q : 8 * (q - 8)) + (lane >> 3);
     const int row = q < 8 ? min(e0 + rr, E - 1) : min(t0 + rr, T - 1);
     voff[i] = (uint32_t)row * (uint32_t)H * 2u + (uint32_t)(((lane & 7) ^ (4 * (q & 1) + (lane >> 4))) * 16);
   }
   auto dma = [&](int s, uint8_t* buf) {
 #pragma unroll
-    for (int i = 0; i < 6; i++) {
-      const int q = 6 * wave + i;
+    for (int i = 0; i < kRouterFills; i++) {
+      const int q = kRouterFills * wave + i;
       buf_load_lds16(q < 8 ? rA : rB, buf + q * 1024, s < nks ? voff[i] : kBufDead, (uint32_t)s * 128u);
     }
   };
@@ -74,24 +80,18 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
 #pragma unroll
   for (int h = 0; h < 2; h++) rdc[h] = rd0 + (uint32_t)((((4 * h + g) ^ (r16 >> 1))) * 16);
 
-  v4f acc[4][2];
+  v4f acc[4];
 #pragma unroll
-  for (int j = 0; j < 4; j++)
-#pragma unroll
-    for (int t = 0; t < 2; t++) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 4; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const uint8_t* buf) {
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      v4i bo[2];
-#pragma unroll
-      for (int t = 0; t < 2; t++) bo[t] = *(const v4i*)(buf + 8 * 1024 + (2 * wave + t) * 2048 + rdc[h]);
+      const v4i bo = *(const v4i*)(buf + 8 * 1024 + wave * 2048 + rdc[h]);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const v4i ao = *(const v4i*)(buf + j * 2048 + rdc[h]);
-#pragma unroll
-        for (int t = 0; t < 2; t++)
-          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_r, ao),
-                                                              __builtin_bit_cast(v8bf_r, bo[t]), acc[j][t], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_r, ao), __builtin_bit_cast(v8bf_r, bo),
+                                                         acc[j], 0, 0, 0);
       }
     }
   };
@@ -102,19 +102,19 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   __builtin_amdgcn_sched_barrier(0);
   int s0 = 0;
   for (; s0 + 3 <= nks; s0 += 3) {
-    MOEFFN_WAIT_VMCNT(6);  // this wave's fill of step s0 has landed (step s0+1's 6 fills may be in flight)
+    MOEFFN_WAIT_VMCNT(kRouterFills);  // this wave's fill of step s0 has landed (step s0+1's may be in flight)
     __builtin_amdgcn_s_barrier();
     dma(s0 + 2, ring2);
     __builtin_amdgcn_sched_barrier(0);
     compute(ring0);
     __builtin_amdgcn_sched_barrier(0);
-    MOEFFN_WAIT_VMCNT(6);
+    MOEFFN_WAIT_VMCNT(kRouterFills);
     __builtin_amdgcn_s_barrier();
     dma(s0 + 3, ring0);
     __builtin_amdgcn_sched_barrier(0);
     compute(ring1);
     __builtin_amdgcn_sched_barrier(0);
-    MOEFFN_WAIT_VMCNT(6);
+    MOEFFN_WAIT_VMCNT(kRouterFills);
     __builtin_amdgcn_s_barrier();
     dma(s0 + 4, ring1);
     __builtin_amdgcn_sched_barrier(0);
@@ -134,23 +134,20 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint16_t* __re
   }
   MOEFFN_WAIT_VMCNT(0);  // no fill outlives the workgroup
 
-  // lane (c = r16, g) holds experts e0 + 16j + 4g .. +3 of token t0 + 32 wave + 16t + c
+  // lane (c = r16, g) holds experts e0 + 16j + 4g .. +3 of token t0 + 16 wave + c
+  const int tok = t0 + 16 * wave + r16;
+  if (tok >= T) return;
 #pragma unroll
-  for (int t = 0; t < 2; t++) {
-    const int tok = t0 + 32 * wave + 16 * t + r16;
-    if (tok >= T) continue;
+  for (int j = 0; j < 4; j++) {
+    if (j >= nblk) continue;
+    const int e = e0 + 16 * j + 4 * g;
+    float* dst = logits + (size_t)tok * E + e;
+    if ((E & 3) == 0 && e + 4 <= E) {
+      stg16f(dst, acc[j]);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      if (j >= nblk) continue;
-      const int e = e0 + 16 * j + 4 * g;
-      float* dst = logits + (size_t)tok * E + e;
-      if ((E & 3) == 0 && e + 4 <= E) {
-        stg16f(dst, acc[j][t]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; i++)
-          if (e + i < E) dst[i] = acc[j][t][i];
-      }
+      for (int i = 0; i < 4; i++)
+        if (e + i < E) dst[i] = acc[j][i];
     }
   }
 }
@@ -259,7 +256,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 hipError_t launch_router(const uint16_t* x, const uint16_t* wg, float* logits, int32_t* idx, float* wts, int T, int H,
                          int E, int k, hipStream_t stream) {
   const dim3 g1((unsigned)((T + kRouterTok - 1) / kRouterTok), (unsigned)((E + kRouterExp - 1) / kRouterExp));
-  hipLaunchKernelGGL(router_logits_kernel, g1, dim3(256), 0, stream, x, wg, logits, T, H, E);
+  hipLaunchKernelGGL(router_logits_kernel, g1, dim3(kRouterThreads), 0, stream, x, wg, logits, T, H, E);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int blocks = (T + 15) / 16;  // 16 tokens per workgroup
