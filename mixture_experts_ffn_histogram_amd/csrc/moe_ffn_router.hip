@@ -9,8 +9,10 @@
 //
 // Two kernels.  router_logits_kernel: a dense bf16 GEMM on
 // v_mfma_f32_16x16x32_bf16; a workgroup computes 128 tokens x 64 experts
-// (8 waves x 16 tokens, two waves per SIMD so one hides the other's waits);
-// both operands are staged through LDS (see below).
+// with 8 waves (two per SIMD, so one hides the other's waits) of 32 tokens x
+// 32 experts each (square wave tiles read the fewest LDS bytes per MFMA: the
+// kernel is bound by LDS reads); both operands are staged through LDS (see
+// below).
 // The gate rows are the A operand, so a lane holds 4 consecutive experts of
 // one token and stores them as one 16-byte piece of the logits row.
 // router_topk_kernel: 16 lanes per token, k rounds of a (value desc, id
@@ -28,12 +30,13 @@ typedef __bf16 v8bf_r __attribute__((ext_vector_type(8)));
 
 constexpr int kRouterTok = 128;                               // tokens per workgroup
 constexpr int kRouterExp = 64;                               // experts per workgroup (4 blocks of 16)
-constexpr int kRouterWaves = 8;                              // 16 tokens per wave
+constexpr int kRouterWaves = 8;                              // 4 token quarters x 2 expert halves
 constexpr int kRouterThreads = 64 * kRouterWaves;
 constexpr int kRouterStage = (kRouterExp + kRouterTok) * 128;  // one 64-element K step: 24 KB
 constexpr int kRouterFills = (kRouterExp + kRouterTok) / 8 / kRouterWaves;  // 8-row fill instructions per wave
-static_assert(kRouterFills * kRouterWaves * 8 == kRouterExp + kRouterTok && kRouterTok == 16 * kRouterWaves,
-              "fills and token blocks must divide evenly over the waves");
+static_assert(kRouterFills * kRouterWaves * 8 == kRouterExp + kRouterTok && kRouterTok == 4 * 32 &&
+                  kRouterExp == 2 * 32 && kRouterWaves == 8,
+              "fills and 32 x 32 wave tiles must divide evenly over the waves");
 
 // Logits tile: 64 gate rows x 128 token rows, both staged through a 3-buffer
 // LDS ring by buffer loads that write LDS directly (fill instruction q holds
@@ -80,19 +83,27 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const uin
 #pragma unroll
   for (int h = 0; h < 2; h++) rdc[h] = rd0 + (uint32_t)((((4 * h + g) ^ (r16 >> 1))) * 16);
 
-  v4f acc[4];
+  // wave tile: token 16-blocks 2 tq, 2 tq + 1 and expert 16-blocks 2 eh, 2 eh + 1
+  const int tq = wave & 3, eh = wave >> 2;
+  v4f acc[2][2];
 #pragma unroll
-  for (int j = 0; j < 4; j++) acc[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 2; j++)
+#pragma unroll
+    for (int t = 0; t < 2; t++) acc[j][t] = v4f{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](const uint8_t* buf) {
 #pragma unroll
     for (int h = 0; h < 2; h++) {
-      const v4i bo = *(const v4i*)(buf + 8 * 1024 + wave * 2048 + rdc[h]);
+      v4i ao[2], bo[2];
 #pragma unroll
-      for (int j = 0; j < 4; j++) {
-        const v4i ao = *(const v4i*)(buf + j * 2048 + rdc[h]);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_r, ao), __builtin_bit_cast(v8bf_r, bo),
-                                                         acc[j], 0, 0, 0);
-      }
+      for (int t = 0; t < 2; t++) bo[t] = *(const v4i*)(buf + 8 * 1024 + (2 * tq + t) * 2048 + rdc[h]);
+#pragma unroll
+      for (int j = 0; j < 2; j++) ao[j] = *(const v4i*)(buf + (2 * eh + j) * 2048 + rdc[h]);
+#pragma unroll
+      for (int j = 0; j < 2; j++)
+#pragma unroll
+        for (int t = 0; t < 2; t++)
+          acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf_r, ao[j]),
+                                                              __builtin_bit_cast(v8bf_r, bo[t]), acc[j][t], 0, 0, 0);
     }
   };
 
@@ -134,20 +145,23 @@ __global__ __launch_bounds__(kRouterThreads) void router_logits_kernel(const uin
   }
   MOEFFN_WAIT_VMCNT(0);  // no fill outlives the workgroup
 
-  // lane (c = r16, g) holds experts e0 + 16j + 4g .. +3 of token t0 + 16 wave + c
-  const int tok = t0 + 16 * wave + r16;
-  if (tok >= T) return;
+  // lane (c = r16, g) holds experts e0 + 16 (2 eh + j) + 4g .. +3 of token t0 + 32 tq + 16t + c
 #pragma unroll
-  for (int j = 0; j < 4; j++) {
-    if (j >= nblk) continue;
-    const int e = e0 + 16 * j + 4 * g;
-    float* dst = logits + (size_t)tok * E + e;
-    if ((E & 3) == 0 && e + 4 <= E) {
-      stg16f(dst, acc[j]);
-    } else {
+  for (int t = 0; t < 2; t++) {
+    const int tok = t0 + 32 * tq + 16 * t + r16;
+    if (tok >= T) continue;
 #pragma unroll
-      for (int i = 0; i < 4; i++)
-        if (e + i < E) dst[i] = acc[j][i];
+    for (int j = 0; j < 2; j++) {
+      if (2 * eh + j >= nblk) continue;
+      const int e = e0 + 16 * (2 * eh + j) + 4 * g;
+      float* dst = logits + (size_t)tok * E + e;
+      if ((E & 3) == 0 && e + 4 <= E) {
+        stg16f(dst, acc[j][t]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; i++)
+          if (e + i < E) dst[i] = acc[j][t][i];
+      }
     }
   }
 }
