@@ -70,7 +70,11 @@ def check(x, wg, k, gl, gi, gw):
 
 
 @pytest.mark.parametrize("T,H,E,k", [(64, 256, 8, 2), (512, 2048, 64, 6), (128, 7168, 256, 8),
-                                     (300, 384, 40, 5), (37, 128, 18, 3), (1, 64, 512, 64), (129, 640, 16, 16)])
+                                     (300, 384, 40, 5), (37, 128, 18, 3), (1, 64, 512, 64), (129, 640, 16, 16),
+                                     # more than 256 experts (32 logits per top-k lane), ragged E, many tokens
+                                     (300, 256, 300, 8), (130, 192, 512, 33),
+                                     # k = 1 (weight exactly 1) and k = E (every expert, full order)
+                                     (200, 256, 20, 1), (70, 128, 24, 24)])
 def test_router_matches_oracle(T, H, E, k):
     log(f"router T={T} H={H} E={E} k={k}")
     x = synth.activations_bf16(T, H, seed=T + H)
