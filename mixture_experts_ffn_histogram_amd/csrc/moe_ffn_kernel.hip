@@ -1375,7 +1375,7 @@ __device__ void phase_wg_tiles(const KParams& p, Shared& sh, SharedB<BM>& sb, co
 // in chunks of kBigGM token blocks x all feature blocks, token block fastest,
 // so the 32 workgroups of one XCD share about 32 / kBigGM weight slices and
 // kBigGM token blocks at a time and fetch each from outside the XCD once.
-constexpr int kBigGM = 4;
+constexpr int kBigGM = 2;
 
 __device__ __forceinline__ int xcc_id() {
   uint32_t v;
