@@ -10,9 +10,8 @@
 // Two kernels.  router_logits_kernel: a dense bf16 GEMM on
 // v_mfma_f32_16x16x32_bf16; a workgroup computes 128 tokens x 64 experts
 // with 8 waves (two per SIMD, so one hides the other's waits) of 32 tokens x
-// 32 experts each (square wave tiles read the fewest LDS bytes per MFMA: the
-// kernel is bound by LDS reads); both operands are staged through LDS (see
-// below).
+// 32 experts each (square wave tiles read the fewest LDS bytes per MFMA);
+// both operands are staged through LDS (see below).
 // The gate rows are the A operand, so a lane holds 4 consecutive experts of
 // one token and stores them as one 16-byte piece of the logits row.
 // router_topk_kernel: 16 lanes per token, k rounds of a (value desc, id
