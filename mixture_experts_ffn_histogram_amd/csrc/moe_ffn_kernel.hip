@@ -1317,17 +1317,18 @@ __device__ __forceinline__ void decode_tile(const Shared& sh, int E, int NB, int
 // Wave-tile phase: every streaming wave claims and processes its own tiles.
 // The claim for the next tile is issued before the current tile starts, so
 // its round trip overlaps the tile's loads.  Three of a workgroup's four
-// waves stream; the fourth goes straight to the next grid barrier.  These
-// tiles stream weights, and with all four waves loading, the texture unit
-// and L2 contention cost more than the extra bytes in flight gain (DeepSeek
-// shape, T=128: 4 streaming waves 1,299 us, 3: 1,256-1,262, 2: 1,255-1,260,
-// 1: 1,868).
-constexpr int kWaveTileWaves = 3;
+// waves stream the L1 tiles and two the L2 tiles; the others go straight to
+// the next grid barrier.  These tiles stream weights, and with all four
+// waves loading, the texture unit and L2 contention cost more than the extra
+// bytes in flight gain (DeepSeek shape, T=128, waves streaming L1 / L2:
+// 4/4 1,299 us, 3/3 1,246-1,262, 2/2 1,255-1,260, 1/1 1,868, 3/4 1,258,
+// 4/3 1,272, 3/2 1,239).
+constexpr int kWaveTileWavesL1 = 3, kWaveTileWavesL2 = 2;
 
 template <int RECIPE, int BM>
 __device__ void phase_wave_tiles(const KParams& p, Shared& sh, const int* lr2s, bool local, bool l1) {
   const int lane = threadIdx.x & 63;
-  if ((threadIdx.x >> 6) >= kWaveTileWaves) return;
+  if ((threadIdx.x >> 6) >= (l1 ? kWaveTileWavesL1 : kWaveTileWavesL2)) return;
   const int E = p.E;
   const int NB = l1 ? p.I / 32 : p.H / 64;
   const uint32_t n = (uint32_t)(sh.mbo[E] * NB);
