@@ -51,7 +51,18 @@ int check_problem(const moe_ffn_problem* p) {
   if (p->num_experts > moeffn::kMaxExperts || p->top_k > moeffn::kMaxTopK) return MOE_FFN_ERR_UNSUPPORTED;
   if (p->hidden > (1 << 20) || p->intermediate > (1 << 20)) return MOE_FFN_ERR_UNSUPPORTED;
   // slot indices are 32-bit
-  if (p->max_tokens * p->top_k + moeffn::kMaxBM >= (int64_t(1) << 31)) return MOE_FFN_ERR_UNSUPPORTED;
+  const int64_t lim = int64_t(1) << 31;
+  if (p->max_tokens * p->top_k + moeffn::kMaxBM >= lim) return MOE_FFN_ERR_UNSUPPORTED;
+  // Every tile kind addresses x rows, h rows (padded by kMaxBM rows) and one
+  // expert's weight matrix with 32-bit byte offsets (buffer ranges and
+  // per-lane offsets): each of these byte ranges must stay below 2^31.
+  const int64_t act = p->recipe == MOE_FFN_RECIPE_BF16 ? 2 : 1;  // bytes per x / h element
+  const int64_t w1_bytes = p->recipe == MOE_FFN_RECIPE_BF16   ? 4 * p->intermediate * p->hidden
+                           : p->recipe == MOE_FFN_RECIPE_FP8_FP8 ? 2 * p->intermediate * p->hidden
+                                                                 : p->intermediate * p->hidden;
+  if (p->max_tokens * p->hidden * act >= lim) return MOE_FFN_ERR_UNSUPPORTED;
+  if ((p->max_tokens * p->top_k + moeffn::kMaxBM) * p->intermediate * act >= lim) return MOE_FFN_ERR_UNSUPPORTED;
+  if (w1_bytes >= lim) return MOE_FFN_ERR_UNSUPPORTED;
   return MOE_FFN_OK;
 }
 
@@ -248,15 +259,11 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   k.o = reinterpret_cast<float*>(ws + L.o);
 
   int bm = choose_block_m(recipe, T, p->top_k, p->num_experts);
-  // 128-row tiles address x, h and one expert's weights with 32-bit buffer offsets
-  const int64_t lim = (int64_t)1 << 31;
-  const bool big_ok = p->max_tokens * p->hidden < lim && (p->max_tokens * p->top_k + 128) * p->intermediate < lim &&
-                      p->intermediate * p->hidden < lim;
   const long bm_env = env_long("MOE_FFN_BLOCK_M", 0);  // tuning override: 16, 32, 64 or 128
   if ((bm_env == 16 || bm_env == 32 || bm_env == 64 || bm_env == 128) && bm_env <= moeffn::max_block_m(recipe))
     bm = (int)bm_env;
   // the 128-row tiles read the K-major weight scales and the tiled weights
-  if (bm == 128 && (!big_ok || !km || !tiled || L.hsg == L.xsg)) bm = 64;
+  if (bm == 128 && (!km || !tiled || L.hsg == L.xsg)) bm = 64;
   if (env_long("MOE_FFN_LOG", 0) > 0)
     std::fprintf(stderr, "moe_ffn: T=%lld recipe=%d grid=%d (CUs %d, reserve %d, cap %d) block_m=%d\n",
                  (long long)T, recipe, grid, cus, reserve, a->max_cus, bm);

@@ -136,6 +136,53 @@ __device__ bool grid_barrier(const KParams& p, int id, Shared& sh) {
   return ok != 0;
 }
 
+// Entry check of the per-call state.  Every word of the control block must be
+// zero when a call starts (the workspace is zeroed once after allocation and
+// every call leaves it zeroed).  Workgroup 0 reads all of it before any
+// workgroup of this call writes to it -- the others wait for its verdict --
+// so the check never sees this call's own counters.  A dirty block is
+// reported once (out_status = DIRTY_WORKSPACE), marked aborted so that no
+// wait of this call can block, and otherwise left as found: every workgroup
+// then skips all work, barriers and the exit reset, and later calls stay
+// dirty until the caller zeroes the workspace.  Returns the verdict (a wait
+// that runs out counts as not clean and raises TIMEOUT).
+constexpr uint32_t kVerdictClean = 1u, kVerdictDirty = 2u;
+
+__device__ uint32_t entry_verdict(const KParams& p, Shared& sh) {
+  const int tid = threadIdx.x;
+  uint32_t* words = reinterpret_cast<uint32_t*>(p.ctrl);
+  if (blockIdx.x == 0) {
+    const uint32_t w = tid < kCtrlWords ? ld_relaxed(words + tid) : 0u;
+    const int nonzero = __syncthreads_or(w != 0u);
+    if (tid == 0) {
+      if (nonzero) {
+        st_relaxed(&p.ctrl->abort, 1u);
+        st_relaxed(&p.ctrl->verdict, kVerdictDirty);
+        if (p.out_status) *p.out_status = ST_DIRTY;
+      } else {
+        st_relaxed(&p.ctrl->verdict, kVerdictClean);
+      }
+    }
+    return nonzero ? kVerdictDirty : kVerdictClean;
+  }
+  if (tid == 0) {
+    uint32_t v;
+    const uint64_t t0 = now_ticks();
+    while ((v = ld_relaxed(&p.ctrl->verdict)) == 0u) {
+      if (now_ticks() - t0 > p.timeout_ticks) {
+        raise_status(p, ST_TIMEOUT, true);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    sh.tile = v;
+  }
+  __syncthreads();
+  const uint32_t v = sh.tile;
+  __syncthreads();
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Routing
 // ---------------------------------------------------------------------------
@@ -1522,18 +1569,7 @@ __device__ __forceinline__ void run_call(const KParams& p, Shared& sh, WaveCount
   const int S = p.T * p.k;
   const bool local = !kBig && S <= kLocalRouteSlots;
 
-  if (tid == 0) {
-    int dirty = 0;
-    if (ld_relaxed(&p.ctrl->exit_count) != 0u && ld_relaxed(&p.ctrl->abort) == 0u) {
-      dirty = 1;
-      raise_status(p, ST_DIRTY, true);
-      if (p.out_status) *p.out_status = ST_DIRTY;
-    }
-    sh.flag = dirty;
-  }
-  __syncthreads();
-  const int dirty = sh.flag;
-  __syncthreads();
+  const int dirty = entry_verdict(p, sh) != kVerdictClean;
 
   if (!dirty) {
     if (local) {
@@ -1560,9 +1596,12 @@ __device__ __forceinline__ void run_call(const KParams& p, Shared& sh, WaveCount
 done:
   fence_release();
   __syncthreads();
-  if (tid == 0) {
+  // A dirty call leaves the control block as it found it (plus the abort
+  // flag and verdict set by workgroup 0): no exit count, no reset.
+  if (tid == 0 && !dirty) {
     const uint32_t old = add_acq_rel(&p.ctrl->exit_count, 1u);
-    if (old == gridDim.x - 1 && !dirty) {
+    // the verdict is re-read: only a call that workgroup 0 found clean resets
+    if (old == gridDim.x - 1 && ld_relaxed(&p.ctrl->verdict) == kVerdictClean) {
       // last workgroup out: every other workgroup is past its last access
       const int st = __hip_atomic_load(&p.ctrl->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (p.out_status) *p.out_status = st;
@@ -1573,6 +1612,7 @@ done:
         for (int r = 0; r < 8; r++) st_relaxed(&p.ctrl->xq[l][r], 0u);
       st_relaxed(&p.ctrl->abort, 0u);
       __hip_atomic_store(&p.ctrl->status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      st_relaxed(&p.ctrl->verdict, 0u);
       st_release(&p.ctrl->exit_count, 0u);
     }
   }

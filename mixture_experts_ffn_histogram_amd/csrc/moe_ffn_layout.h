@@ -29,13 +29,16 @@ struct Ctrl {
   uint32_t abort;              // set on a fatal condition: every wait gives up
   int32_t status;              // first MOE_FFN_STATUS_* of the call
   uint32_t xq[2][8];           // 128-row tiles: per-XCD range claim counters (L1, L2)
-  uint32_t pad[37];
+  uint32_t verdict;            // workgroup 0's entry check of this block: 0 none yet, 1 clean, 2 dirty
+  uint32_t pad[36];
 };
 static_assert(sizeof(Ctrl) == 256, "control block must stay 256 bytes");
 static_assert(offsetof(Ctrl, bar) == 0, "barrier counters lead the control block");
 static_assert(offsetof(Ctrl, exit_count) == 24, "layout change must be deliberate");
 static_assert(offsetof(Ctrl, status) == 40, "layout change must be deliberate");
 static_assert(offsetof(Ctrl, xq) == 44, "layout change must be deliberate");
+static_assert(offsetof(Ctrl, verdict) == 108, "layout change must be deliberate");
+constexpr int kCtrlWords = (int)(sizeof(Ctrl) / 4);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

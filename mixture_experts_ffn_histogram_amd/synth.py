@@ -15,6 +15,8 @@ Recipe (what each tensor looks like):
     drawn with probabilities FP4_MAG_PROBS, uniform sign; scale byte per
     block 127 + round(log2(sigma / FP4_STD)) + j, j as for e4m3.
   * bf16 tensors: bf16 cast of N(0, sigma^2).
+  * x of a config with x_bf16 set (the FP8 x FP8 workload): bf16 N(0, 1),
+    quantised on the fly by the pre-dispatch quantiser (e4m3 + e8m0 1x32).
   * routing "softmax": logits N(0,1) [T,E] -> softmax -> top-k (descending)
     -> weights renormalised over the k picks.
   * routing "uniform": k distinct experts per token, uniformly at random;
@@ -58,6 +60,7 @@ class Config:
     y_fp32: bool = False
     zipf_s: float = 1.2
     empty_frac: float = 0.1
+    x_bf16: bool = False    # x drawn as bf16 N(0, 1), to be quantised by the pre-dispatch quantiser
     extra: dict = field(default_factory=dict, compare=False)
 
     def with_(self, **kw) -> "Config":
@@ -69,7 +72,7 @@ CONFIGS = {
     "bf16_T64_H256_I128_E8_k2": Config("bf16_T64_H256_I128_E8_k2", RECIPE_BF16, 64, 256, 128, 8, 2,
                                        "softmax", 101, y_fp32=True),
     "fp8xfp8_T512_H2048_I768_E64_k6": Config("fp8xfp8_T512_H2048_I768_E64_k6", RECIPE_FP8_FP8, 512, 2048, 768,
-                                             64, 6, "uniform", 202),
+                                             64, 6, "uniform", 202, x_bf16=True),
     "deepseek_fp8xfp4_T128": Config("deepseek_fp8xfp4_T128", RECIPE_FP8_FP4, 128, 7168, 2048, 256, 8,
                                     "softmax", 303),
     "deepseek_fp8xfp4_T8192_zipf": Config("deepseek_fp8xfp4_T8192_zipf", RECIPE_FP8_FP4, 8192, 7168, 2048, 256, 8,
@@ -205,15 +208,24 @@ def routing(cfg: Config, T: int | None = None):
 
 
 def activations(cfg: Config, T: int | None = None):
-    """x [T,H] codes and x_sf [T,H/32] (None for bf16)."""
+    """x [T,H] codes and x_sf [T,H/32] (None for bf16; both None when the
+    config draws bf16 x for on-the-fly quantisation: see x_bf16_of)."""
     T = cfg.T if T is None else T
     H = cfg.H
     rng = _rng(cfg.seed, _TID["x"], T)
     if cfg.recipe == RECIPE_BF16:
         return _bf16_bits(rng, (T, H), 1.0), None
+    if cfg.x_bf16:
+        return None, None
     x = _e4m3_codes(rng, (T, H))
     x_sf = _scale_bytes(_rng(cfg.seed, _TID["x_sf"], T), (T, H // 32), int(round(math.log2(1.0 / 64.0))))
     return x, x_sf
+
+
+def x_bf16_of(cfg: Config, T: int | None = None) -> np.ndarray:
+    """x ~ N(0, 1) as bf16 bit patterns [T, H] (configs whose x is quantised on the fly)."""
+    T = cfg.T if T is None else T
+    return _bf16_bits(_rng(cfg.seed, _TID["x"], T, 16), (T, cfg.H), 1.0)
 
 
 def activations_bf16(T: int, H: int, seed: int) -> np.ndarray:
@@ -244,7 +256,8 @@ def make_problem(cfg: Config, T: int | None = None, threads: int = 8, weights=No
     else:
         w1, w1_sf, w2, w2_sf = weights
     return {"name": cfg.name, "T": T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "k": cfg.k, "recipe": cfg.recipe,
-            "x": x, "x_sf": x_sf, "topk_idx": idx, "topk_weights": w,
+            "x": x, "x_sf": x_sf, "x_bf16": x_bf16_of(cfg, T) if cfg.x_bf16 else None,
+            "topk_idx": idx, "topk_weights": w,
             "w1": w1, "w1_sf": w1_sf, "w2": w2, "w2_sf": w2_sf,
             "clamp": cfg.clamp, "y_fp32": cfg.y_fp32}
 
@@ -259,5 +272,5 @@ def with_inputs(p: dict, cfg: Config, seed: int) -> dict:
     x, x_sf = activations(c2, p["T"])
     idx, w = routing(c2, p["T"])
     q = dict(p)
-    q.update(x=x, x_sf=x_sf, topk_idx=idx, topk_weights=w)
+    q.update(x=x, x_sf=x_sf, x_bf16=x_bf16_of(c2, p["T"]) if c2.x_bf16 else None, topk_idx=idx, topk_weights=w)
     return q

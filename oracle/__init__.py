@@ -69,6 +69,7 @@ def lib():
             ("oracle_forward", ctypes.c_int, [P] + [P] * 14),
             ("oracle_forward_tokens", ctypes.c_int, [P] + [P] * 8 + [P, i64, P]),
             ("oracle_forward_tokens_band", ctypes.c_int, [P] + [P] * 8 + [P, i64, P, d, P]),
+            ("oracle_forward_tokens_rows", ctypes.c_int, [P] + [P] * 8 + [P, i64, P, d, P, P]),
             ("oracle_ffn_row", ctypes.c_int, [P, P, P, i64, i64, P, P, P, P, P, P, P, P, P, P, d, P]),
             ("oracle_num_threads", ctypes.c_int, []),
             ("oracle_quantize_act", ctypes.c_int, [P, i64, i64, P, P]),
@@ -190,6 +191,27 @@ def forward_tokens_band(p: dict, tokens, y_fp32: bool, clamp: float, rho: float)
     if rc < 0:
         raise RuntimeError(f"oracle_forward_tokens_band failed: {rc}")
     return y, allow, rc
+
+
+def forward_tokens_rows(p: dict, tokens, y_fp32: bool, clamp: float, rho: float):
+    """Per-token forward of the listed tokens that also returns, for every slot
+    j of listed token q, the re-quantised activation values of that routed row
+    (hq[q, j, :]) and the rounding-decision band of each for `rho`
+    (delta[q, j, :]); masked slots keep NaN rows.  Returns (y_rows, hq, delta,
+    status)."""
+    T, H, I, E, k, recipe = p["T"], p["H"], p["I"], p["E"], p["k"], p["recipe"]
+    x, x_sf, idx, w, w1, w1_sf, w2, w2_sf = _args(p)
+    toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
+    y = np.zeros((len(toks), H), np.float32 if y_fp32 else np.uint16)
+    hq = np.full((len(toks), k, I), np.nan, np.float64)
+    delta = np.full((len(toks), k, I), np.nan, np.float64)
+    prob = _problem(T, H, I, E, k, recipe, y_fp32, clamp)
+    rc = lib().oracle_forward_tokens_rows(ctypes.byref(prob), _ptr(x), _ptr(x_sf), _ptr(idx), _ptr(w),
+                                          _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
+                                          _ptr(toks), len(toks), _ptr(y), float(rho), _ptr(hq), _ptr(delta))
+    if rc < 0:
+        raise RuntimeError(f"oracle_forward_tokens_rows failed: {rc}")
+    return y, hq, delta, rc
 
 
 def ffn_row(p: dict, t: int, e: int, clamp: float, rho: float = 0.0):

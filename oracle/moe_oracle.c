@@ -408,6 +408,17 @@ static void store_y(const oracle_problem* p, void* y, int64_t yrow, int64_t n, d
     else ((uint16_t*)y)[yrow * p->hidden + n] = oracle_enc_bf16(oracle_round_bf16(acc));
 }
 
+/* Inputs the forward reads must be present when there are tokens to process. */
+static int check_inputs(const oracle_problem* p, const void* x, const uint8_t* x_sf, const int32_t* topk_idx,
+                        const float* topk_w, const void* w1, const uint8_t* w1_sf, const void* w2,
+                        const uint8_t* w2_sf) {
+    int fp8 = p->recipe != OR_RECIPE_BF16;
+    if (p->num_tokens == 0) return OR_OK;
+    if (!x || !topk_idx || !topk_w || !w1 || !w2) return OR_BAD_ARG;
+    if (fp8 && (!x_sf || !w1_sf || !w2_sf)) return OR_BAD_ARG;
+    return OR_OK;
+}
+
 static int check_problem(const oracle_problem* p) {
     if (!p) return OR_BAD_ARG;
     if (p->num_tokens < 0 || p->hidden <= 0 || p->intermediate <= 0 || p->num_experts <= 0 || p->top_k <= 0) return OR_BAD_ARG;
@@ -433,6 +444,7 @@ int oracle_forward(const oracle_problem* p, const void* x, const uint8_t* x_sf,
     float* o;
     int rc, err = 0;
     if (check_problem(p) != OR_OK) return OR_BAD_ARG;
+    if (check_inputs(p, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf) != OR_OK) return OR_BAD_ARG;
     T = p->num_tokens; H = p->hidden; E = p->num_experts; k = p->top_k;
     counts = (int32_t*)malloc(sizeof(int32_t) * (size_t)E);
     offsets = (int32_t*)malloc(sizeof(int32_t) * (size_t)(E + 1));
@@ -484,15 +496,16 @@ int oracle_forward(const oracle_problem* p, const void* x, const uint8_t* x_sf,
  * sum_j |w_j| * sum_i delta_i |W2(e_j, n, i)|: the largest change of y that
  * re-quantisation decisions inside the band `rho` can cause (requant_band).
  */
-int oracle_forward_tokens_band(const oracle_problem* p, const void* x, const uint8_t* x_sf,
+static int forward_tokens_impl(const oracle_problem* p, const void* x, const uint8_t* x_sf,
                                const int32_t* topk_idx, const float* topk_w,
                                const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
                                const int64_t* tokens, int64_t ntok, void* y_rows,
-                               double rho, double* allow_rows) {
-    int64_t H, E, k, q;
+                               double rho, double* allow_rows, double* hq_rows, double* delta_rows) {
+    int64_t H, I, E, k, q;
     int err = 0, bad = 0;
     if (check_problem(p) != OR_OK) return OR_BAD_ARG;
-    H = p->hidden; E = p->num_experts; k = p->top_k;
+    if (check_inputs(p, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf) != OR_OK) return OR_BAD_ARG;
+    H = p->hidden; I = p->intermediate; E = p->num_experts; k = p->top_k;
     for (q = 0; q < ntok; q++)
         if (tokens[q] < 0 || tokens[q] >= p->num_tokens) return OR_BAD_ARG;
 #pragma omp parallel for schedule(dynamic, 1) reduction(|:err) reduction(|:bad)
@@ -504,8 +517,10 @@ int oracle_forward_tokens_band(const oracle_problem* p, const void* x, const uin
         for (j = 0; j < k; j++) {
             int32_t e = topk_idx[t * k + j];
             if (e >= 0 && e < E) {
-                if (ffn_row(p, x, x_sf, t, e, w1, w1_sf, w2, w2_sf, NULL, NULL, NULL, NULL, NULL, o + j * H,
-                            rho, oa ? oa + j * H : NULL, NULL) != OR_OK) err |= 1;
+                if (ffn_row(p, x, x_sf, t, e, w1, w1_sf, w2, w2_sf, NULL, NULL,
+                            hq_rows ? hq_rows + (q * k + j) * I : NULL, NULL, NULL, o + j * H,
+                            rho, oa ? oa + j * H : NULL, delta_rows ? delta_rows + (q * k + j) * I : NULL) != OR_OK)
+                    err |= 1;
             } else if (e != -1) {
                 bad |= 1;
             }
@@ -527,6 +542,29 @@ int oracle_forward_tokens_band(const oracle_problem* p, const void* x, const uin
     }
     if (err) return OR_NO_MEMORY;
     return bad ? OR_BAD_EXPERT_INDEX : OR_OK;
+}
+
+int oracle_forward_tokens_band(const oracle_problem* p, const void* x, const uint8_t* x_sf,
+                               const int32_t* topk_idx, const float* topk_w,
+                               const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
+                               const int64_t* tokens, int64_t ntok, void* y_rows,
+                               double rho, double* allow_rows) {
+    return forward_tokens_impl(p, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, tokens, ntok, y_rows, rho,
+                               allow_rows, NULL, NULL);
+}
+
+/* Per-token forward that also hands back, for slot j of listed token q (row
+   q*k + j of hq_rows / delta_rows, each [ntok*k, I]), the re-quantised
+   activation values of that routed row and the rounding-decision band of each
+   of them for `rho` (requant_band; zero for the BF16 recipe).  Rows of masked
+   slots are left untouched.  For unit checks of an implementation's h. */
+int oracle_forward_tokens_rows(const oracle_problem* p, const void* x, const uint8_t* x_sf,
+                               const int32_t* topk_idx, const float* topk_w,
+                               const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
+                               const int64_t* tokens, int64_t ntok, void* y_rows,
+                               double rho, double* hq_rows, double* delta_rows) {
+    return forward_tokens_impl(p, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, tokens, ntok, y_rows, rho,
+                               NULL, hq_rows, delta_rows);
 }
 
 int oracle_forward_tokens(const oracle_problem* p, const void* x, const uint8_t* x_sf,

@@ -44,7 +44,7 @@ extern "C" {
 // stream is not used: the runtime rejected a mask holding CUs of only some
 // XCDs.)  Returns 0 on success and stores an opaque handle.
 int side_start(int blocks, int ms, void** handle) {
-  if (blocks < 1 || blocks > 7 || ms < 1 || ms > 2000) return -7;
+  if (blocks < 1 || blocks > 7 || ms < 1 || ms > 10000) return -7;
   Side* s = new Side{};
   if (hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) != hipSuccess) { delete s; return -1; }
   if (hipMalloc(&s->done, 8 * sizeof(uint32_t)) != hipSuccess) { delete s; return -2; }

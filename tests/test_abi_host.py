@@ -85,6 +85,41 @@ def test_problem_validation(dims, code):
     assert ei.value.code == code
 
 
+# Byte ranges the tiles address with 32-bit offsets must stay below 2^31:
+# x rows (max_tokens * H * elem), h rows ((max_tokens * k + 128) * I * elem)
+# and one expert's W1 (2I * H * weight bytes).  Each case sits on one side of
+# one of these limits.
+@pytest.mark.parametrize("dims,ok", [
+    # DeepSeek shape: the h rows bind first, (T*8 + 128) * 2048 < 2^31 <=> T <= 131055
+    ((131055, 7168, 2048, 256, 8, mf.RECIPE_FP8_FP4), True),
+    ((131056, 7168, 2048, 256, 8, mf.RECIPE_FP8_FP4), False),
+    # x rows bind: BF16 x, T * 4096 * 2 < 2^31 <=> T <= 262143
+    ((262143, 4096, 64, 8, 1, mf.RECIPE_BF16), True),
+    ((262144, 4096, 64, 8, 1, mf.RECIPE_BF16), False),
+    # e4m3 x: T * 8192 < 2^31 <=> T <= 262143
+    ((262143, 8192, 128, 8, 1, mf.RECIPE_FP8_FP8), True),
+    ((262144, 8192, 128, 8, 1, mf.RECIPE_FP8_FP8), False),
+    # h rows of BF16: (T*2 + 128) * 8192 * 2 < 2^31 <=> T <= 65471
+    ((65471, 256, 8192, 8, 2, mf.RECIPE_BF16), True),
+    ((65472, 256, 8192, 8, 2, mf.RECIPE_BF16), False),
+    # one expert's W1: e2m1 I * H, e4m3 2 * I * H, bf16 4 * I * H bytes
+    ((16, 65536, 32640, 8, 2, mf.RECIPE_FP8_FP4), True),
+    ((16, 65536, 32768, 8, 2, mf.RECIPE_FP8_FP4), False),
+    ((16, 32768, 32640, 8, 2, mf.RECIPE_FP8_FP8), True),
+    ((16, 32768, 32768, 8, 2, mf.RECIPE_FP8_FP8), False),
+    ((16, 16384, 32704, 8, 2, mf.RECIPE_BF16), True),
+    ((16, 16384, 32768, 8, 2, mf.RECIPE_BF16), False),
+])
+def test_problem_32bit_offset_limits(dims, ok):
+    prob = mf.make_problem(*dims)
+    if ok:
+        assert mf.get_workspace_size(prob) > 0
+    else:
+        with pytest.raises(mf.MoeFFNError) as ei:
+            mf.get_workspace_size(prob)
+        assert ei.value.code == mf.ERR_UNSUPPORTED
+
+
 def _args(**kw):
     a = mf.Args()
     a.num_tokens = kw.get("num_tokens", 4)

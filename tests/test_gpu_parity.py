@@ -1,9 +1,11 @@
 """GPU parity of the HIP forward against the CPU oracle (MI355X only).
 
-Routing outputs must match bit for bit; y must stay within the bounds
-max|y - y_ref| <= 2e-2 RMS(y_ref) (FP8 recipes) and 5e-3 RMS(y_ref) (BF16,
-fp32 y), y_ref being the oracle's rounded output.  Every call goes through
-the C ABI (moe_ffn_forward) via the Python binding.
+Routing outputs must match bit for bit.  y: BF16 recipe within 5e-3 RMS(y_ref)
+(fp32 y); FP8 recipes (gpu_common.fp8_parity): the fp32 y within 2e-2
+RMS(y_ref) plus the effect of the re-quantisation flips the GPU actually made
+(every flipped code checked against the oracle's rounding-decision band), and
+the bf16 y bitwise the rounding of the fp32 y.  Every call goes through the C
+ABI (moe_ffn_forward) via the Python binding.
 """
 import numpy as np
 import pytest
@@ -11,8 +13,8 @@ import torch
 
 import oracle
 from mixture_experts_ffn_histogram_amd import synth
-from gpu_common import (Runner, assert_h_decisions, assert_y_parity, check_tables, log, oracle_y, oracle_y_band,
-                        rel_err, tol_for, upload_inputs)
+from gpu_common import (Runner, check_tables, fp8_parity, log, oracle_y, quantize_on_the_fly, rel_err,
+                        upload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -65,18 +67,17 @@ def test_bf16_recipe_full(y_fp32):
 
 
 def test_fp8xfp8_config_full():
+    # x ~ N(0, 1) quantised on the fly: GPU quantiser for the call, oracle quantiser for the oracle
     cfg = synth.CONFIGS["fp8xfp8_T512_H2048_I768_E64_k6"]
     p = synth.make_problem(cfg, threads=8)
     log("fp8xfp8 T512 full")
     run = Runner(p)
+    quantize_on_the_fly(p, run)
     run.run()
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     _check_tables(run, p, p["T"])
-    ref, allow = oracle_y_band(p, False, p["clamp"])
-    assert_y_parity(run.y_float(), ref, allow, 2e-2, "fp8xfp8 T512")
-    flips = assert_h_decisions(run, p, range(0, p["T"] * p["k"], 97), p["clamp"])
-    log(f"  near-tie code flips in sampled rows: {flips}")
+    fp8_parity(run, p, "fp8xfp8 T512 (C2)")
 
 
 @pytest.mark.parametrize("T,E,k,prepared", [(64, 32, 8, True), (96, 32, 8, True), (40, 8, 4, True),
@@ -93,11 +94,7 @@ def test_fp8xfp4_reduced_full(T, E, k, prepared):
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     _check_tables(run, p, T)
-    ref, allow = oracle_y_band(p, False, p["clamp"])
-    assert_y_parity(run.y_float(), ref, allow, 2e-2, f"fp8xfp4 T={T}")
-    R = int(run.offsets[-1].item())
-    flips = assert_h_decisions(run, p, list(range(0, R, max(1, R // 40))) + [R - 1], p["clamp"])
-    log(f"  near-tie code flips in sampled rows: {flips}")
+    fp8_parity(run, p, f"fp8xfp4 T={T} E={E} k={k} prepared={prepared}")
 
 
 @pytest.mark.parametrize("T,H,I,E,k", [
@@ -115,26 +112,20 @@ def test_fp8xfp4_block128_shapes(T, H, I, E, k, monkeypatch):
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     _check_tables(run, p, T)
-    ref, allow = oracle_y_band(p, False, p["clamp"])
-    assert_y_parity(run.y_float(), ref, allow, 2e-2, f"block 128 T={T}")
-    R = int(run.offsets[-1].item())
-    assert_h_decisions(run, p, list(range(0, R, max(1, R // 30))) + [R - 1], p["clamp"])
+    fp8_parity(run, p, f"block 128 T={T} H={H} I={I}")
 
 
-def test_deepseek_T128_sampled():
+def test_deepseek_T128_all_tokens():
+    # the whole call at the DeepSeek shape (C3): all 128 tokens, all 1024 routed rows' codes
     cfg = synth.CONFIGS["deepseek_fp8xfp4_T128"]
     p = synth.make_problem(cfg, threads=16)
-    log("deepseek T128 (full shape), sampled tokens")
+    log("deepseek T128 (full shape), all tokens")
     run = Runner(p)
     run.run()
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     _check_tables(run, p, p["T"])
-    toks = [0, 1, 2, 63, 64, 100, 126, 127] + list(np.random.default_rng(0).choice(128, 8, replace=False))
-    ref, allow = oracle_y_band(p, False, p["clamp"], tokens=toks)
-    assert_y_parity(run.y_float()[toks], ref, allow, 2e-2, "deepseek T128")
-    flips = assert_h_decisions(run, p, [0, 100, 511, 777, 1023], p["clamp"])
-    log(f"  near-tie code flips in sampled rows: {flips}")
+    fp8_parity(run, p, "deepseek T128 (C3)")
 
 
 def test_deterministic_and_grid_size_invariant():
@@ -164,8 +155,7 @@ def test_bad_expert_index_reported_and_masked():
     q = dict(p, topk_idx=p["topk_idx"].copy())
     q["topk_idx"][(q["topk_idx"] < -1) | (q["topk_idx"] >= 8)] = -1
     _check_tables(run, q, 64)
-    ref, allow = oracle_y_band(q, False, p["clamp"])
-    assert_y_parity(run.y_float(), ref, allow, 2e-2, "bad index")
+    fp8_parity(run, q, "bad index", status=1)
     # the next call on the same workspace is clean
     p2 = dict(q)
     run.p = p2
@@ -179,14 +169,11 @@ def test_num_tokens_below_capacity_leaves_tail_rows():
     cfg = _small_cfg(synth.RECIPE_FP8_FP4, 200, 512, 256, 8, 2, "softmax", seed=11)
     p = synth.make_problem(cfg, threads=4)
     run = Runner(p)
-    run.run(num_tokens=77)
-    torch.cuda.synchronize()
-    assert bool((run.y[77:] == -12345).all())
     q = dict(p, T=77, x=p["x"][:77], x_sf=p["x_sf"][:77], topk_idx=p["topk_idx"][:77],
              topk_weights=p["topk_weights"][:77])
+    fp8_parity(run, q, "T=77 of 200", num_tokens=77)
+    assert bool((run.y[77:] == -12345).all()) and bool((run.y32[77:] == -12345).all())
     _check_tables(run, q, 77)
-    ref, allow = oracle_y_band(q, False, p["clamp"])
-    assert_y_parity(run.y_float(77), ref, allow, 2e-2, "T=77 of 200")
 
 
 def test_clamp_engaged_and_off():
@@ -196,11 +183,7 @@ def test_clamp_engaged_and_off():
     run = Runner(p)
     for c in (7.0, 0.0):
         log(f"clamp {c}")
-        run.run(clamp=c)
-        torch.cuda.synchronize()
-        ref, allow = oracle_y_band(p, False, c)
-        assert_y_parity(run.y_float(), ref, allow, 2e-2, f"clamp {c}")
-        assert_h_decisions(run, p, range(0, 128, 9), c)
+        fp8_parity(run, p, f"clamp {c}", clamp=c)
 
 
 def test_graph_replay_changed_inputs_matches_eager():
@@ -233,8 +216,7 @@ def test_graph_replay_changed_inputs_matches_eager():
         assert st == 0
         assert torch.equal(y_graph, run.y), f"replay {r} differs from eager"
         _check_tables(run, q, q["T"])
-        ref, allow = oracle_y_band(q, False, q["clamp"])
-        assert_y_parity(run.y_float(), ref, allow, 2e-2, f"replay {r}")
+        fp8_parity(run, q, f"replay {r}")
 
 
 @pytest.mark.parametrize("E,rows,kb", [(3, 8, 3), (2, 256, 12), (2, 4096, 224), (1, 7168, 64)])
@@ -273,16 +255,39 @@ def test_large_call_without_kmajor_scales_uses_64_row_tiles(monkeypatch):
     p = synth.make_problem(cfg, threads=8)
     log("block 128 requested, no K-major scales")
     run = Runner(p, kmajor=False)
+    fp8_parity(run, p, "no K-major scales")
+    y64 = run.y.clone()
+    run_km = Runner(p)
+    fp8_parity(run_km, p, "K-major scales")
+    log(f"  64-row vs 128-row tiles: {int((y64 != run_km.y).sum())} of {y64.numel()} y elements differ in the last bit")
+
+
+# Control-block words (32-bit) of the workspace: bar[0..5], exit_count 6,
+# tile_next 7, tile_next2 8, abort 9, status 10, xq 11..26, verdict 27, pad 28..63.
+@pytest.mark.parametrize("word,value", [(6, 5), (6, 1 << 30), (2, 1), (9, 1), (27, 1), (50, 7)])
+def test_dirty_workspace_reported_without_waiting(word, value):
+    import time
+    cfg = _small_cfg(synth.RECIPE_FP8_FP4, 64, 256, 128, 8, 2, "softmax", seed=17)
+    p = synth.make_problem(cfg, threads=4)
+    run = Runner(p)
     run.run()
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
-    _check_tables(run, p, p["T"])
-    ref, allow = oracle_y_band(p, False, p["clamp"])
-    assert_y_parity(run.y_float(), ref, allow, 2e-2, "no K-major scales")
-    y64 = run.y.clone()
-    run_km = Runner(p)
-    run_km.run()
+    y_ref = run.y.clone()
+    ctrl = run.m.workspace[:256].view(torch.int32)
+    ctrl[word] = value
     torch.cuda.synchronize()
-    assert int(run_km.status.item()) == 0
-    assert_y_parity(run_km.y_float(), ref, allow, 2e-2, "K-major scales")
-    log(f"  64-row vs 128-row tiles: {int((y64 != run_km.y).sum())} of {y64.numel()} y elements differ in the last bit")
+    log(f"dirty control word {word} = {value}")
+    for _ in range(2):   # the block stays dirty until the caller zeroes it
+        t0 = time.time()
+        run.run()
+        torch.cuda.synchronize()
+        dt = time.time() - t0
+        assert int(run.status.item()) == 3, f"status {int(run.status.item())}"
+        assert dt < 0.5, f"dirty call took {dt:.2f} s (a wait ran into its timeout)"
+    run.m.workspace.zero_()
+    run.run()
+    torch.cuda.synchronize()
+    assert int(run.status.item()) == 0
+    assert torch.equal(run.y, y_ref)
+    assert not bool(run.m.workspace[:256].any()), "a clean call must leave the control block zeroed"

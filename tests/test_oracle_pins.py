@@ -240,7 +240,7 @@ def test_gemms_exact_rationals(recipe):
 
 
 def test_requant_row_codes_decode_to_hq_and_obey_scale_rule():
-    cfg = synth.CONFIGS["fp8xfp8_T512_H2048_I768_E64_k6"].with_(T=4)
+    cfg = synth.CONFIGS["fp8xfp8_T512_H2048_I768_E64_k6"].with_(T=4, x_bf16=False)
     p = synth.make_problem(cfg.with_(E=4, H=256, I=128), threads=1)
     row = oracle.ffn_row(p, 2, 1, 7.0)
     codes = torch.from_numpy(row["h_codes"]).view(torch.float8_e4m3fn).double().numpy()
@@ -456,3 +456,23 @@ def test_band_is_monotone_zero_at_zero_and_absent_for_bf16():
     assert np.all(allow == 0.0)
     row = oracle.ffn_row(p, 0, int(p["topk_idx"][0, 0]), 7.0, rho=2.0 ** -8)
     assert np.all((row["delta"] == 0.0) | (row["delta"] > 0.0))
+
+
+def test_forward_tokens_rows_hands_back_each_slots_row():
+    # the per-slot rows (re-quantised values and bands) are those of the slot's
+    # own (token, expert) pair, in (listed token, slot) order; masked slots stay NaN
+    p = _small(synth.RECIPE_FP8_FP4, T=8)
+    p["topk_idx"][3, 1] = -1
+    toks = [6, 1, 3]
+    y, hq, delta, rc = oracle.forward_tokens_rows(p, toks, True, 7.0, 2.0 ** -8)
+    assert rc == oracle.OK
+    assert np.array_equal(y, oracle.forward_tokens(p, toks, True, 7.0)[0])
+    for q, t in enumerate(toks):
+        for j in range(p["k"]):
+            e = int(p["topk_idx"][t, j])
+            if e < 0:
+                assert np.all(np.isnan(hq[q, j])) and np.all(np.isnan(delta[q, j]))
+                continue
+            row = oracle.ffn_row(p, t, e, 7.0, rho=2.0 ** -8)
+            assert np.array_equal(hq[q, j], row["hq"]) and np.array_equal(delta[q, j], row["delta"])
+    assert np.nanmax(delta) > 0.0
