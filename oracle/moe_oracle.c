@@ -244,40 +244,57 @@ static double e4m3_spacing(double v) {
 
 /* Rounding-decision band (parity infrastructure, not part of the method).
    The re-quantisation turns the fp32 activation into a code.  An
-   implementation whose L1 outputs differ from the exact ones by at most
-   rho * RMS(L1 row) per element sees each activation move by at most
-   band_i = rho * RMS * (1.1 |u_i| + |silu(g_i)|)   (|silu'| <= 1.1),
-   so it may pick the other grid neighbour of an element whose exact value
-   lies within band_i of a rounding midpoint, and the other block exponent
-   when the block amax lies within the largest band of the block of a
-   boundary 448 * 2^E.  delta[i] receives the largest resulting change of the
-   dequantised value: one grid spacing, two spacings at the coarser exponent
-   for an ambiguous block exponent, 0 for an unambiguous element. */
-static void requant_band(const float* h, const float* c, int64_t I, double rho, float clamp, double* delta) {
+   implementation whose L1 outputs differ from the exact ones sees each
+   activation move, and may pick another code for an element whose exact
+   value lies close to a rounding midpoint (or another block exponent when the
+   block amax lies close to a boundary 448 * 2^E).  The error model is the
+   one of a blocked contraction: the K dimension is summed in steps of 128
+   elements, each step with an error of at most rho times the step's largest
+   |product|, and the step results are added in fp32 (at most 2^-24 times the
+   sum of |products| per addition).  So L1 output n is off by at most
+     eps[n] = rho * S[n] + steps * 2^-24 * A[n],
+     S[n] = sum over steps of max |x_k w_nk|,  A[n] = sum_k |x_k w_nk|,
+   and, the clamp being 1-Lipschitz and |silu'| <= 1.1, activation i by at most
+     band_i = 1.1 * eps_g * (|u| + eps_u) + |silu(g)| * eps_u
+   (g, u the clamped gate and up values, eps_g = eps[i], eps_u = eps[I+i]).
+   delta[i] receives the largest change of the dequantised value such a
+   deviation can cause: 0 when no rounding midpoint lies within band_i of the
+   exact activation and the block exponent is unambiguous, else band_i plus one
+   grid spacing at |h_i| + band_i, taken at the coarsest block exponent the
+   block amax (within its largest band) can select. */
+static double e4m3_spacing_at(double v, int E) {   /* grid spacing at |v| for block exponent E, in v's units */
+    double q = ldexp(fabs(v), -E);
+    return ldexp(e4m3_spacing(q > 448.0 ? 448.0 : q), E);
+}
+
+static void requant_band(const float* h, const float* c, const double* eps, int64_t I, float clamp, double* delta) {
     int64_t b, i;
-    double rms = 0.0, cc = clamp;
+    double cc = clamp;
     int clamp_on = isfinite(cc) && cc > 0.0;
-    for (i = 0; i < 2 * I; i++) rms += (double)c[i] * (double)c[i];
-    rms = sqrt(rms / (double)(2 * I));
     for (b = 0; b < I / 32; b++) {
         double amax = 0.0, bmax = 0.0, band[32];
-        int E, scale_amb;
+        int E, Ehi, scale_amb;
         for (i = 32 * b; i < 32 * b + 32; i++) {
-            double g = c[i], u = c[I + i];
+            double g = c[i], u = c[I + i], eg = eps[i], eu = eps[I + i];
             if (clamp_on) { g = fmin(fmax(g, -cc), cc); u = fmin(fmax(u, -cc), cc); }
-            band[i - 32 * b] = rho * rms * (1.1 * fabs(u) + fabs(g / (1.0 + exp(-g))));
+            band[i - 32 * b] = 1.1 * eg * (fabs(u) + eu) + fabs(g / (1.0 + exp(-g))) * eu;
             if (band[i - 32 * b] > bmax) bmax = band[i - 32 * b];
             if (fabs((double)h[i]) > amax) amax = fabs((double)h[i]);
         }
         E = oracle_scale_exp(amax);
-        scale_amb = amax > 0.0 && (fabs(amax - ldexp(448.0, E)) <= bmax || fabs(amax - ldexp(448.0, E - 1)) <= bmax);
+        Ehi = oracle_scale_exp(amax + bmax);
+        if (amax > 0.0)
+            scale_amb = Ehi != E || oracle_scale_exp(amax - bmax > 0.0 ? amax - bmax : 0.0) != E;
+        else
+            scale_amb = bmax > 0.0;
         for (i = 32 * b; i < 32 * b + 32; i++) {
             double q = ldexp((double)h[i], -E);
             double sp = e4m3_spacing(q);
             double lo = floor(q / sp) * sp;       /* grid neighbours of q (exact: sp is a power of two) */
             double mid = lo + 0.5 * sp;
-            if (scale_amb) delta[i] = 2.0 * ldexp(e4m3_spacing(ldexp((double)h[i], -(E + 1))), E + 1);
-            else if (ldexp(fabs(q - mid), E) <= band[i - 32 * b]) delta[i] = ldexp(sp, E);
+            double bd = band[i - 32 * b];
+            if (scale_amb) delta[i] = bd + e4m3_spacing_at(fabs((double)h[i]) + bd, Ehi);
+            else if (ldexp(fabs(q - mid), E) <= bd) delta[i] = bd + e4m3_spacing_at(fabs((double)h[i]) + bd, E);
             else delta[i] = 0.0;
         }
     }
@@ -299,11 +316,26 @@ static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
         return OR_NO_MEMORY;
     }
     /* O3: L1 = x_t . W1[e]^T over the hidden dimension, exact in double,
-       rounded once to fp32 (fp32 accumulator of the grouped GEMM). */
+       rounded once to fp32 (fp32 accumulator of the grouped GEMM).  With a
+       band requested, also the error bound eps[n] of requant_band. */
+    const int want_band = (o_allow || delta_out) && p->recipe != OR_RECIPE_BF16;
+    double* eps = want_band ? (double*)calloc((size_t)(2 * I), sizeof(double)) : NULL;
+    if (want_band && !eps) { free(xd); free(wd); free(c); free(h); free(hq); return OR_NO_MEMORY; }
     dequant_act_row(p->recipe, x, x_sf, t, H, xd);
     for (n = 0; n < 2 * I; n++) {
         dequant_weight_row(p->recipe, w1, w1_sf, e * 2 * I + n, H, wd);
         c[n] = (float)dot(xd, wd, H);
+        if (eps) {
+            double S = 0.0, A = 0.0, m = 0.0;
+            int64_t k, steps = (H + 127) / 128;
+            for (k = 0; k < H; k++) {
+                double a = fabs(xd[k] * wd[k]);
+                A += a;
+                if (a > m) m = a;
+                if (k % 128 == 127 || k == H - 1) { S += m; m = 0.0; }
+            }
+            eps[n] = rho * S + (double)steps * ldexp(A, -24);
+        }
     }
     /* O4: rows [0, I) of W1 are the gate, rows [I, 2I) the up projection. */
     for (i = 0; i < I; i++) h[i] = oracle_swiglu(c[i], c[I + i], p->activation_clamp);
@@ -332,10 +364,10 @@ static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
        rounded once to fp32 (the per-slot result stays fp32 until the combine). */
     {
         double* delta = NULL;
-        if ((o_allow || delta_out) && p->recipe != OR_RECIPE_BF16) {
+        if (want_band) {
             delta = (double*)calloc((size_t)I, sizeof(double));
-            if (!delta) { free(xd); free(wd); free(c); free(h); free(hq); return OR_NO_MEMORY; }
-            requant_band(h, c, I, rho, p->activation_clamp, delta);
+            if (!delta) { free(xd); free(wd); free(c); free(h); free(hq); free(eps); return OR_NO_MEMORY; }
+            requant_band(h, c, eps, I, p->activation_clamp, delta);
         }
         for (n = 0; n < H; n++) {
             dequant_weight_row(p->recipe, w2, w2_sf, e * H + n, I, wd);
@@ -353,6 +385,7 @@ static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
         }
         free(delta);
     }
+    free(eps);
     if (c_out) memcpy(c_out, c, sizeof(float) * (size_t)(2 * I));
     if (h_out) memcpy(h_out, h, sizeof(float) * (size_t)I);
     if (hq_out) memcpy(hq_out, hq, sizeof(double) * (size_t)I);
