@@ -46,6 +46,21 @@ extern "C" {
 #define MOE_FFN_RECIPE_FP8_FP8 1  /* x, W e4m3 + e8m0 per 1x32 along K; h e4m3 + e8m0     */
 #define MOE_FFN_RECIPE_FP8_FP4 2  /* x e4m3, W e2m1 (packed), e8m0 per 1x32 along K       */
 
+/* Storage layout of the weights (moe_ffn_problem.weight_layout):
+   ROW_MAJOR: w1 [E, 2I, H] and w2 [E, H, I] row-major (K contiguous; e2m1 packs
+     element 2j in the low nibble of byte j), scales [E, rows, K/32] row-major.
+     Every recipe.  Large e2m1 calls run on 64-row token blocks.
+   TILED (e2m1 recipe only; the production layout of the e2m1 weights, prepared
+     once per set of weights by moe_ffn_transform_weights and
+     moe_ffn_transform_weight_scales): per expert, the weight matrix [rows, K]
+     stored as 1 KB tiles of 16 rows x one 128-element K stage in MFMA operand
+     order, and its scales as groups of four K stages per 16-row block (exact
+     offsets at the two transforms).  Same sizes as ROW_MAJOR; the caller holds
+     this one copy.  Every token-block size, including the 128-row tiles of
+     large calls, reads it with whole-tile loads. */
+#define MOE_FFN_WEIGHTS_ROW_MAJOR 0
+#define MOE_FFN_WEIGHTS_TILED 1
+
 /* Output element type of y. */
 #define MOE_FFN_Y_BF16 0
 #define MOE_FFN_Y_FP32 1
@@ -62,10 +77,16 @@ extern "C" {
 #define MOE_FFN_STATUS_BAD_EXPERT_INDEX 1   /* an index outside [-1, E) was masked (y still valid) */
 #define MOE_FFN_STATUS_TIMEOUT 2            /* a grid barrier / readiness wait exceeded its bound; */
                                             /* y is undefined; the workspace is left clean         */
-#define MOE_FFN_STATUS_DIRTY_WORKSPACE 3    /* counters were non-zero at entry; zero the workspace */
+#define MOE_FFN_STATUS_DIRTY_WORKSPACE 3    /* the control block was not zero at entry: the call   */
+                                            /* did nothing and left it so; zero the workspace      */
 
 /* Problem: fixes the workspace size and layout.  It does not depend on the
-   CU count or the reserve (digest: buffer cache key excludes the SM count). */
+   CU count or the reserve (digest: buffer cache key excludes the SM count).
+   The tiles address x rows, h rows and one expert's weight matrix with 32-bit
+   byte offsets: a problem with max_tokens*H*a, (max_tokens*k + 128)*I*a
+   (a = 2 for BF16, else 1) or one expert's W1 bytes (2I*H times 2, 1 or 1/2)
+   at or above 2^31 is MOE_FFN_ERR_UNSUPPORTED (DeepSeek shape, k = 8:
+   max_tokens <= 131055). */
 typedef struct {
     int64_t max_tokens;   /* capacity of x / y / topk rows (>= num_tokens of any call)         */
     int64_t hidden;       /* H: multiple of 128 (64 for BF16)                                  */
@@ -73,7 +94,7 @@ typedef struct {
     int64_t num_experts;  /* E: 1..512                                                         */
     int64_t top_k;        /* k: 1..64                                                          */
     int32_t recipe;       /* MOE_FFN_RECIPE_*                                                  */
-    int32_t reserved_;    /* must be 0                                                         */
+    int32_t weight_layout; /* MOE_FFN_WEIGHTS_* (TILED only with MOE_FFN_RECIPE_FP8_FP4)        */
 } moe_ffn_problem;
 
 /* Per-call arguments.  Shapes use T = num_tokens. */
@@ -83,10 +104,11 @@ typedef struct {
     const uint8_t* x_sf;         /* [T, H/32] e8m0; NULL for BF16                                   */
     const int32_t* topk_idx;     /* [T, k] expert ids; -1 masks a slot                              */
     const float* topk_weights;   /* [T, k] combine weights                                          */
-    const void* w1;              /* [E, 2I, H] (e2m1: [E, 2I, H/2] bytes); rows [0,I) gate, [I,2I) up */
-    const uint8_t* w1_sf;        /* [E, 2I, H/32] e8m0; NULL for BF16                               */
-    const void* w2;              /* [E, H, I] (e2m1: [E, H, I/2] bytes)                             */
-    const uint8_t* w2_sf;        /* [E, H, I/32] e8m0; NULL for BF16                                */
+    const void* w1;              /* [E, 2I, H] (e2m1: [E, 2I, H/2] bytes); rows [0,I) gate, [I,2I) up; */
+                                 /* in the problem's weight_layout                                   */
+    const uint8_t* w1_sf;        /* [E, 2I, H/32] e8m0 (or its TILED order); NULL for BF16           */
+    const void* w2;              /* [E, H, I] (e2m1: [E, H, I/2] bytes), in the weight_layout       */
+    const uint8_t* w2_sf;        /* [E, H, I/32] e8m0 (or its TILED order); NULL for BF16           */
     void* y;                     /* [T, H] of y_dtype; rows >= T untouched                          */
     int32_t y_dtype;             /* MOE_FFN_Y_*                                                      */
     float activation_clamp;      /* finite and > 0: clamp gate and up to [-c, c]; else no clamp      */
@@ -98,17 +120,6 @@ typedef struct {
     int32_t* row_to_slot;        /* optional [T*k] device out: first R = offsets[E] entries written  */
     int32_t* slot_to_row;        /* optional [T*k] device out: row of each slot, -1 when masked      */
     int32_t* status;             /* optional device int: MOE_FFN_STATUS_* of this call               */
-    const uint8_t* w1_sf_kmajor; /* optional, e2m1 recipe: w1_sf in K-major order [E, H/32, 2I], as   */
-                                 /* written by moe_ffn_transform_weight_scales; NULL = not given      */
-    const uint8_t* w2_sf_kmajor; /* optional, e2m1 recipe: w2_sf as [E, I/32, H]; NULL = not given   */
-                                 /* The 128-row tiles of large calls need both K-major copies (their */
-                                 /* per-stage scale fills then read contiguous rows); without them a */
-                                 /* large e2m1 call runs on 64-row tiles.  Both must hold the same   */
-                                 /* values as w1_sf / w2_sf.                                          */
-    const void* w1_tiled;        /* optional, e2m1 recipe: w1 as written by moe_ffn_transform_weights */
-    const void* w2_tiled;        /* (rows = 2I, k_bytes = H/2) / (rows = H, k_bytes = I/2); NULL =    */
-                                 /* not given.  The 128-row tiles need both (with the K-major scale   */
-                                 /* copies); they must hold the same weights as w1 / w2.              */
 } moe_ffn_args;
 
 /* Bytes of device workspace one in-flight call needs (buffer-size query of the
@@ -129,16 +140,21 @@ int moe_ffn_get_token_alignment(int32_t recipe, int64_t* alignment);
 int moe_ffn_forward(const moe_ffn_problem* problem, const moe_ffn_args* args,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Weight-scale transform (the weight transform step of the pages' host API,
-   done once per set of weights): dst[e][b][r] = src[e][r][b] for e <
-   num_experts, r < rows, b < k_blocks, i.e. the e8m0 scales of each expert's
-   weight matrix re-ordered K-major.  For W1 rows = 2I, k_blocks = H/32; for
-   W2 rows = H, k_blocks = I/32.  src and dst are device buffers of
-   num_experts*rows*k_blocks bytes that must not overlap; dst must be 4-byte
-   aligned.  Enqueued on `stream` (a hipStream_t; NULL = default stream);
-   asynchronous, allocates nothing.  Returns MOE_FFN_ERR_INVALID_ARG for null
-   pointers, non-positive sizes, rows not a multiple of 4 or a misaligned
-   dst, MOE_FFN_ERR_HIP when the launch fails. */
+/* Weight-scale transform to the TILED layout (the weight transform step of
+   the pages' host API, done once per set of weights).  src: the row-major e8m0
+   scales [num_experts, rows, k_blocks] of one weight matrix (W1: rows = 2I,
+   k_blocks = H/32; W2: rows = H, k_blocks = I/32); with nk = k_blocks/4 K
+   stages of 128 elements, row r = 16b + i, stage s = 4G + u, 32-block c < 4:
+     dst[e*rows*k_blocks + (b*nk + 4G)*64 + i*4*n + u*4 + c] = src[e][r][4s + c],
+     n = min(4, nk - 4G) (the stages in group G),
+   i.e. per 16-row block, groups of four K stages, each group [16 rows][n
+   stages][4 blocks]: one 16-byte load brings a row's scales for four stages,
+   one 64-byte run a stage's scales for 16 rows.  src and dst: device buffers
+   of num_experts*rows*k_blocks bytes, 4-byte aligned, not overlapping.
+   Enqueued on `stream` (a hipStream_t; NULL = default stream); asynchronous,
+   allocates nothing.  Returns MOE_FFN_ERR_INVALID_ARG for null or misaligned
+   pointers, non-positive sizes, rows not a multiple of 16 or k_blocks not a
+   multiple of 4, MOE_FFN_ERR_HIP when the launch fails. */
 int moe_ffn_transform_weight_scales(const uint8_t* src, uint8_t* dst, int64_t num_experts, int64_t rows,
                                     int64_t k_blocks, void* stream);
 
@@ -193,15 +209,16 @@ int moe_ffn_route_topk(const void* x_bf16, const void* w_gate_bf16, int64_t num_
                        int64_t num_experts, int64_t top_k, float* logits, int32_t* topk_idx, float* topk_weights,
                        void* stream);
 
-/* Weight transform for the e2m1 recipe (the weight transform step of the
-   pages' host API, done once per set of weights): re-orders each expert's
-   packed e2m1 weight matrix [rows, k_bytes] into tiles of 16 rows x 64 bytes
-   (one 128-element K stage), each tile 1 KB in MFMA operand order:
+/* Weight transform to the TILED layout for the e2m1 recipe (the weight
+   transform step of the pages' host API, done once per set of weights):
+   re-orders each expert's packed e2m1 weight matrix [rows, k_bytes] into tiles
+   of 16 rows x 64 bytes (one 128-element K stage), each tile 1 KB in MFMA
+   operand order:
      dst[((e*(rows/16) + b) * (k_bytes/64) + s) * 1024 + (g*16 + r) * 16 + c]
        = src[(e*rows + 16b + r) * k_bytes + 64s + 16g + c]
-   for r < 16, g < 4, c < 16.  The 128-row tiles then load one contiguous
-   1 KB piece per 16 weight rows and K stage.  For W1 rows = 2I, k_bytes =
-   H/2; for W2 rows = H, k_bytes = I/2.  src and dst: device buffers of
+   for r < 16, g < 4, c < 16.  The GEMM tiles then load one contiguous 1 KB
+   piece per 16 weight rows and K stage.  For W1 rows = 2I, k_bytes = H/2; for
+   W2 rows = H, k_bytes = I/2.  src and dst: device buffers of
    num_experts*rows*k_bytes bytes, 16-byte aligned, not overlapping.  Enqueued
    on `stream` (a hipStream_t; NULL = default stream); asynchronous,
    allocates nothing.  Returns MOE_FFN_ERR_INVALID_ARG for null or misaligned

@@ -16,6 +16,8 @@ LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
 RECIPE_BF16 = 0
 RECIPE_FP8_FP8 = 1
 RECIPE_FP8_FP4 = 2
+WEIGHTS_ROW_MAJOR = 0
+WEIGHTS_TILED = 1
 Y_BF16 = 0
 Y_FP32 = 1
 
@@ -33,7 +35,7 @@ STATUS_DIRTY_WORKSPACE = 3
 class Problem(ctypes.Structure):
     _fields_ = [("max_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
                 ("intermediate", ctypes.c_int64), ("num_experts", ctypes.c_int64),
-                ("top_k", ctypes.c_int64), ("recipe", ctypes.c_int32), ("reserved_", ctypes.c_int32)]
+                ("top_k", ctypes.c_int64), ("recipe", ctypes.c_int32), ("weight_layout", ctypes.c_int32)]
 
 
 class Args(ctypes.Structure):
@@ -47,9 +49,7 @@ class Args(ctypes.Structure):
                 ("reserved_cus", ctypes.c_int32), ("max_cus", ctypes.c_int32),
                 ("expert_counts", ctypes.c_void_p), ("expert_offsets", ctypes.c_void_p),
                 ("row_to_slot", ctypes.c_void_p), ("slot_to_row", ctypes.c_void_p),
-                ("status", ctypes.c_void_p),
-                ("w1_sf_kmajor", ctypes.c_void_p), ("w2_sf_kmajor", ctypes.c_void_p),
-                ("w1_tiled", ctypes.c_void_p), ("w2_tiled", ctypes.c_void_p)]
+                ("status", ctypes.c_void_p)]
 
 
 class WorkspaceView(ctypes.Structure):
@@ -113,8 +113,9 @@ def _check(code: int, what: str) -> int:
 
 
 def make_problem(max_tokens: int, hidden: int, intermediate: int, num_experts: int, top_k: int,
-                 recipe: int) -> Problem:
-    return Problem(int(max_tokens), int(hidden), int(intermediate), int(num_experts), int(top_k), int(recipe), 0)
+                 recipe: int, weight_layout: int = WEIGHTS_ROW_MAJOR) -> Problem:
+    return Problem(int(max_tokens), int(hidden), int(intermediate), int(num_experts), int(top_k), int(recipe),
+                   int(weight_layout))
 
 
 def get_workspace_size(problem: Problem) -> int:
@@ -148,7 +149,8 @@ def _ptr(t):
 
 
 def transform_weight_scales(src, dst, num_experts: int, rows: int, k_blocks: int, stream=None) -> None:
-    """Enqueue moe_ffn_transform_weight_scales: dst[e][b][r] = src[e][r][b] (uint8 device tensors)."""
+    """Enqueue moe_ffn_transform_weight_scales: row-major e8m0 scales [E, rows, k_blocks] -> the TILED
+    layout (uint8 device tensors)."""
     import torch
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -190,16 +192,6 @@ def route_topk(x_bf16, w_gate_bf16, logits, topk_idx, topk_weights, stream=None)
     _check(rc, "moe_ffn_route_topk")
 
 
-def kmajor_weight_scales(w1_sf, w2_sf, num_experts: int, hidden: int, intermediate: int, stream=None):
-    """K-major copies of W1's and W2's scales (new device tensors), for the 128-row tiles."""
-    import torch
-    a = torch.empty_like(w1_sf)
-    b = torch.empty_like(w2_sf)
-    transform_weight_scales(w1_sf, a, num_experts, 2 * intermediate, hidden // 32, stream)
-    transform_weight_scales(w2_sf, b, num_experts, hidden, intermediate // 32, stream)
-    return a, b
-
-
 def transform_weights(src, dst, num_experts: int, rows: int, k_bytes: int, stream=None) -> None:
     """Enqueue moe_ffn_transform_weights: tiled copy of packed e2m1 weights (uint8 device tensors)."""
     import torch
@@ -210,21 +202,23 @@ def transform_weights(src, dst, num_experts: int, rows: int, k_bytes: int, strea
     _check(rc, "moe_ffn_transform_weights")
 
 
-def tiled_weights(w1, w2, num_experts: int, hidden: int, intermediate: int, stream=None):
-    """Tiled copies of the packed e2m1 W1 and W2 (new device tensors), for the 128-row tiles."""
+def tile_weights(w1, w1_sf, w2, w2_sf, num_experts: int, hidden: int, intermediate: int, stream=None):
+    """The e2m1 weights and their scales in the TILED layout (four new device tensors, same shapes
+    and sizes as the row-major ones): the storage a problem with weight_layout=WEIGHTS_TILED takes."""
     import torch
-    a = torch.empty_like(w1)
-    b = torch.empty_like(w2)
-    transform_weights(w1, a, num_experts, 2 * intermediate, hidden // 2, stream)
-    transform_weights(w2, b, num_experts, hidden, intermediate // 2, stream)
-    return a, b
+    w1t, w2t = torch.empty_like(w1), torch.empty_like(w2)
+    s1t, s2t = torch.empty_like(w1_sf), torch.empty_like(w2_sf)
+    transform_weights(w1, w1t, num_experts, 2 * intermediate, hidden // 2, stream)
+    transform_weights(w2, w2t, num_experts, hidden, intermediate // 2, stream)
+    transform_weight_scales(w1_sf, s1t, num_experts, 2 * intermediate, hidden // 32, stream)
+    transform_weight_scales(w2_sf, s2t, num_experts, hidden, intermediate // 32, stream)
+    return w1t, s1t, w2t, s2t
 
 
 def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, topk_weights,
             w1, w1_sf, w2, w2_sf, y, y_dtype: int, activation_clamp: float,
             reserved_cus: int = -1, max_cus: int = 0, expert_counts=None, expert_offsets=None,
-            row_to_slot=None, slot_to_row=None, status=None, stream=None, w1_sf_kmajor=None,
-            w2_sf_kmajor=None, w1_tiled=None, w2_tiled=None) -> None:
+            row_to_slot=None, slot_to_row=None, status=None, stream=None) -> None:
     """Enqueue moe_ffn_forward on `stream` (default: torch's current stream).
 
     All tensors are device tensors laid out as include/moe_ffn.h states; the
@@ -237,8 +231,7 @@ def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, 
     a = Args(int(num_tokens), _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),
              _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf), _ptr(y), int(y_dtype), float(activation_clamp),
              int(reserved_cus), int(max_cus), _ptr(expert_counts), _ptr(expert_offsets),
-             _ptr(row_to_slot), _ptr(slot_to_row), _ptr(status), _ptr(w1_sf_kmajor), _ptr(w2_sf_kmajor),
-             _ptr(w1_tiled), _ptr(w2_tiled))
+             _ptr(row_to_slot), _ptr(slot_to_row), _ptr(status))
     rc = lib().moe_ffn_forward(ctypes.byref(problem), ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                ctypes.c_void_p(stream.cuda_stream))
@@ -248,9 +241,10 @@ def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, 
 class MoeFFN:
     """Owns a problem description and its zero-initialised workspace."""
 
-    def __init__(self, max_tokens, hidden, intermediate, num_experts, top_k, recipe, device="cuda"):
+    def __init__(self, max_tokens, hidden, intermediate, num_experts, top_k, recipe, device="cuda",
+                 weight_layout=WEIGHTS_ROW_MAJOR):
         import torch
-        self.problem = make_problem(max_tokens, hidden, intermediate, num_experts, top_k, recipe)
+        self.problem = make_problem(max_tokens, hidden, intermediate, num_experts, top_k, recipe, weight_layout)
         self.workspace_bytes = get_workspace_size(self.problem)
         self.workspace = torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=device)
         self.recipe = recipe

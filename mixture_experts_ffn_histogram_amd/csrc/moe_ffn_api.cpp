@@ -44,8 +44,10 @@ int check_problem(const moe_ffn_problem* p) {
   if (!p) return MOE_FFN_ERR_INVALID_ARG;
   if (p->max_tokens < 0 || p->hidden <= 0 || p->intermediate <= 0 || p->num_experts <= 0 || p->top_k <= 0)
     return MOE_FFN_ERR_INVALID_ARG;
-  if (p->reserved_ != 0) return MOE_FFN_ERR_INVALID_ARG;
   if (p->recipe < MOE_FFN_RECIPE_BF16 || p->recipe > MOE_FFN_RECIPE_FP8_FP4) return MOE_FFN_ERR_INVALID_ARG;
+  if (p->weight_layout != MOE_FFN_WEIGHTS_ROW_MAJOR && p->weight_layout != MOE_FFN_WEIGHTS_TILED)
+    return MOE_FFN_ERR_INVALID_ARG;
+  if (p->weight_layout == MOE_FFN_WEIGHTS_TILED && p->recipe != MOE_FFN_RECIPE_FP8_FP4) return MOE_FFN_ERR_UNSUPPORTED;
   const int64_t kmul = p->recipe == MOE_FFN_RECIPE_BF16 ? 64 : 128;
   if (p->hidden % kmul || p->intermediate % kmul) return MOE_FFN_ERR_UNSUPPORTED;
   if (p->num_experts > moeffn::kMaxExperts || p->top_k > moeffn::kMaxTopK) return MOE_FFN_ERR_UNSUPPORTED;
@@ -120,8 +122,10 @@ int moe_ffn_get_workspace_view(const moe_ffn_problem* p, moe_ffn_workspace_view*
 
 int moe_ffn_transform_weight_scales(const uint8_t* src, uint8_t* dst, int64_t num_experts, int64_t rows,
                                     int64_t k_blocks, void* stream) {
-  if (!src || !dst || num_experts <= 0 || rows <= 0 || k_blocks <= 0 || rows % 4 != 0) return MOE_FFN_ERR_INVALID_ARG;
-  if ((reinterpret_cast<uintptr_t>(dst) & 3u) != 0) return MOE_FFN_ERR_INVALID_ARG;
+  if (!src || !dst || num_experts <= 0 || rows <= 0 || k_blocks <= 0 || rows % 16 != 0 || k_blocks % 4 != 0)
+    return MOE_FFN_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) & 3u) != 0 || (reinterpret_cast<uintptr_t>(dst) & 3u) != 0)
+    return MOE_FFN_ERR_INVALID_ARG;
   const hipError_t e = moeffn::launch_transform_scales(src, dst, num_experts, rows, k_blocks,
                                                        static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
@@ -196,10 +200,7 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   if (a->y_dtype != MOE_FFN_Y_BF16 && a->y_dtype != MOE_FFN_Y_FP32) return MOE_FFN_ERR_INVALID_ARG;
   if (!a->w1 || !a->w2 || !aligned16(a->w1) || !aligned16(a->w2)) return MOE_FFN_ERR_INVALID_ARG;
   if (!bf16 && (!a->w1_sf || !a->w2_sf || !aligned16(a->w1_sf) || !aligned16(a->w2_sf))) return MOE_FFN_ERR_INVALID_ARG;
-  const bool km = recipe == MOE_FFN_RECIPE_FP8_FP4 && a->w1_sf_kmajor && a->w2_sf_kmajor;
-  if (km && (!aligned16(a->w1_sf_kmajor) || !aligned16(a->w2_sf_kmajor))) return MOE_FFN_ERR_INVALID_ARG;
-  const bool tiled = recipe == MOE_FFN_RECIPE_FP8_FP4 && a->w1_tiled && a->w2_tiled;
-  if (tiled && (!aligned16(a->w1_tiled) || !aligned16(a->w2_tiled))) return MOE_FFN_ERR_INVALID_ARG;
+  const bool tiled = p->weight_layout == MOE_FFN_WEIGHTS_TILED;
   if (T > 0) {
     if (!a->x || !a->topk_idx || !a->topk_weights || !a->y) return MOE_FFN_ERR_INVALID_ARG;
     if (!aligned16(a->x) || !aligned16(a->y) || !aligned16(a->topk_idx) || !aligned16(a->topk_weights))
@@ -238,10 +239,7 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   k.w1_sf = a->w1_sf;
   k.w2 = static_cast<const uint8_t*>(a->w2);
   k.w2_sf = a->w2_sf;
-  k.w1_sf_km = km ? a->w1_sf_kmajor : nullptr;
-  k.w2_sf_km = km ? a->w2_sf_kmajor : nullptr;
-  k.w1_t = tiled ? static_cast<const uint8_t*>(a->w1_tiled) : nullptr;
-  k.w2_t = tiled ? static_cast<const uint8_t*>(a->w2_tiled) : nullptr;
+  k.tiled = tiled ? 1 : 0;
   k.y = a->y;
   k.out_counts = a->expert_counts;
   k.out_offsets = a->expert_offsets;
@@ -262,8 +260,8 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   const long bm_env = env_long("MOE_FFN_BLOCK_M", 0);  // tuning override: 16, 32, 64 or 128
   if ((bm_env == 16 || bm_env == 32 || bm_env == 64 || bm_env == 128) && bm_env <= moeffn::max_block_m(recipe))
     bm = (int)bm_env;
-  // the 128-row tiles read the K-major weight scales and the tiled weights
-  if (bm == 128 && (!km || !tiled || L.hsg == L.xsg)) bm = 64;
+  // the 128-row tiles read the TILED weight layout (and the stage-major scale copies of the workspace)
+  if (bm == 128 && (!tiled || L.hsg == L.xsg)) bm = 64;
   if (env_long("MOE_FFN_LOG", 0) > 0)
     std::fprintf(stderr, "moe_ffn: T=%lld recipe=%d grid=%d (CUs %d, reserve %d, cap %d) block_m=%d\n",
                  (long long)T, recipe, grid, cus, reserve, a->max_cus, bm);
@@ -272,7 +270,7 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
     k.hsg = reinterpret_cast<uint32_t*>(ws + L.hsg);
     k.sg_rows = (int32_t)L.h_rows;
   }
-  const hipError_t err = moeffn::launch_forward(recipe, bm, grid, k, static_cast<hipStream_t>(stream));
+  const hipError_t err = moeffn::launch_forward(recipe, bm, tiled, grid, k, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 

@@ -14,6 +14,7 @@ struct KParams {
   int32_t y_fp32;
   int32_t clamp_on;
   float clamp;
+  int32_t tiled;           // weights (and their scales) in the TILED layout (e2m1 recipe)
   uint64_t timeout_ticks;  // bound on every wait, in 100 MHz realtime ticks
   int64_t chunk_slots;     // routing chunk size
   // inputs
@@ -25,10 +26,6 @@ struct KParams {
   const uint8_t* w1_sf;
   const uint8_t* w2;
   const uint8_t* w2_sf;
-  const uint8_t* w1_sf_km;  // K-major copies of the weight scales (128-row tiles)
-  const uint8_t* w2_sf_km;
-  const uint8_t* w1_t;      // tiled copies of the e2m1 weights (128-row tiles)
-  const uint8_t* w2_t;
   void* y;
   // optional outputs
   int32_t* out_counts;
@@ -53,15 +50,17 @@ struct KParams {
 };
 
 // Launches the persistent kernel for `recipe` with token block `bm` on `grid`
-// workgroups.  Returns the hipError_t of the launch.
-hipError_t launch_forward(int recipe, int bm, int grid, const KParams& p, hipStream_t stream);
+// workgroups, reading the weights in the TILED layout when `tiled` (e2m1
+// recipe).  Returns the hipError_t of the launch.
+hipError_t launch_forward(int recipe, int bm, bool tiled, int grid, const KParams& p, hipStream_t stream);
 
 // e2m1 weights [E][rows][kbytes] -> tiled: per 16-row block and 64-byte K stage one 1 KB piece in
 // MFMA lane order (lane g*16 + r holds row r, bytes 16g .. 16g+15 of the stage).
 hipError_t launch_transform_weights(const uint8_t* src, uint8_t* dst, int64_t E, int64_t rows, int64_t kbytes,
                                     hipStream_t stream);
 
-// dst[e][b][r] = src[e][r][b] (e < E, r < rows, b < kb): weight scales re-ordered K-major.
+// Row-major e8m0 weight scales [E][rows][kb] -> the TILED layout: per 16-row block, groups of four
+// 128-element K stages, each group [16 rows][stages in the group][4 blocks].
 hipError_t launch_transform_scales(const uint8_t* src, uint8_t* dst, int64_t E, int64_t rows, int64_t kb,
                                    hipStream_t stream);
 

@@ -385,10 +385,14 @@ __device__ __forceinline__ int find_expert(const int* mbo, int E, int nb, int t)
 // One tile: expert e, token block mb (BM routed rows), feature block nb.
 // L1: 4 waves x (32 gate + 32 up rows) = 128 intermediate features;
 // L2: 4 waves x 64 rows = 256 hidden outputs.
-template <int RECIPE, int BM>
+// TILED (e2m1 weights in the TILED layout): a wave's weight rows of a K stage
+// are one contiguous 1 KB piece per 16-row block, already in operand order,
+// and a lane's stage scales one dword of its row's group of four stages.
+template <int RECIPE, int BM, bool TILED>
 __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const int* lr2s, bool local, bool l1, int e, int mb,
                           int nb) {
   using C = Cfg<RECIPE, BM>;
+  static_assert(!TILED || RECIPE == 2, "the TILED layout holds e2m1 weights");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, r16 = lane & 15;
   const int H = p.H, I = p.I;
   const int row0 = sh.off[e] + mb * BM;
@@ -436,13 +440,21 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
   const uint8_t* sptr[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    const size_t r = (size_t)(active ? arow[j] + r16 : r16);  // inactive waves stream a valid dummy row
-    size_t lane_off;
-    if constexpr (C::kW4) lane_off = (size_t)g * 16;          // e2m1: elements g*32..g*32+31
-    else if constexpr (C::kBF16) lane_off = (size_t)g * 32;   // bf16: elements g*16..g*16+15
-    else lane_off = (size_t)g * 16;                           // e4m3: bytes g*16 and 64+g*16
-    aptr[j] = W + r * wrow_bytes + lane_off;
-    sptr[j] = C::kBF16 ? nullptr : Wsf + r * wsf_row;
+    if constexpr (TILED) {
+      // 16-row block of this row block (inactive waves stream block 0): weights at (blk * nk + s) KB,
+      // scales of stage s at (blk * nk + 4 * (s / 4)) * 64 + r16 * 4 * n(s) + (s % 4) * 4
+      const size_t blk = (size_t)(active ? arow[j] >> 4 : 0);
+      aptr[j] = W + blk * (size_t)nk * 1024 + (size_t)lane * 16;
+      sptr[j] = Wsf + blk * (size_t)nk * 64;
+    } else {
+      const size_t r = (size_t)(active ? arow[j] + r16 : r16);  // inactive waves stream a valid dummy row
+      size_t lane_off;
+      if constexpr (C::kW4) lane_off = (size_t)g * 16;          // e2m1: elements g*32..g*32+31
+      else if constexpr (C::kBF16) lane_off = (size_t)g * 32;   // bf16: elements g*16..g*16+15
+      else lane_off = (size_t)g * 16;                           // e4m3: bytes g*16 and 64+g*16
+      aptr[j] = W + r * wrow_bytes + lane_off;
+      sptr[j] = C::kBF16 ? nullptr : Wsf + r * wsf_row;
+    }
   }
   __syncthreads();  // boff / bsfoff visible
 
@@ -464,7 +476,11 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
 #pragma unroll
     for (int j = 0; j < 4; j++) {
       const size_t kb = (size_t)ks * 128;  // 128 bytes of a bf16 row per stage, 64 of e2m1, 128 of e4m3
-      if constexpr (C::kW4) {
+      if constexpr (TILED) {
+        ar[slot][j][0] = load16<C::kStream>(aptr[j] + (size_t)ks * 1024);
+        const int g4 = ks & ~3, n = min(4, nk - g4);
+        sar[slot][j] = ldg4(sptr[j] + (size_t)g4 * 64 + (size_t)(r16 * 4 * n + (ks & 3) * 4));
+      } else if constexpr (C::kW4) {
         ar[slot][j][0] = load16<C::kStream>(aptr[j] + (size_t)ks * 64);
       } else if constexpr (C::kBF16) {
         ar[slot][j][0] = load16<C::kStream>(aptr[j] + kb);
@@ -473,7 +489,7 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
         ar[slot][j][0] = load16<C::kStream>(aptr[j] + kb);
         ar[slot][j][1] = load16<C::kStream>(aptr[j] + kb + 64);
       }
-      if constexpr (!C::kBF16) sar[slot][j] = ldg4(sptr[j] + (size_t)ks * 4);
+      if constexpr (!C::kBF16 && !TILED) sar[slot][j] = ldg4(sptr[j] + (size_t)ks * 4);
     }
   };
   auto load_b = [&](int slot, int ks) {
@@ -874,8 +890,8 @@ struct BigRing {
 template <int NT>
 __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __restrict__ B1, uint8_t* __restrict__ B2,
                                           v4f (&acc)[4][NT], rsrc_t rW, uint32_t a_off, const uint32_t (&a_soff)[4],
-                                          rsrc_t rWs, uint32_t as_off, uint32_t ws_stride, uint32_t sa_base,
-                                          const int (&sa_j)[4], rsrc_t rX, const uint32_t (&xoff)[4],
+                                          rsrc_t rWs, uint32_t as_full, uint32_t as_last, uint32_t sa_base,
+                                          rsrc_t rX, const uint32_t (&xoff)[4],
                                           uint32_t brd0, uint32_t brd1, rsrc_t rXs, uint32_t xs_off, uint32_t xs_stride,
                                           int nk, int wave,
                                           int lane) {
@@ -904,10 +920,10 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
   // (wave w issues q = RP*w .. RP*w + RP-1; brd0/brd1 address a lane's MFMA
   // operand bytes 0-15 / 16-31 of routed-row block 0), the routed-row scale dwords (waves
   // beyond the first copy load zeros from past the end of the buffer into
-  // further copies, so every wave issues the same count) and the weight-row
-  // scales of the stage from the K-major copy: wave w fetches block 4s+w of
-  // the tile's 256 weight rows (contiguous runs of 128 or 256 bytes), stored
-  // as [block][tile row].
+  // further copies, so every wave issues the same count) and the scales of
+  // the wave's own 64 weight rows from the TILED layout: lane l fetches the
+  // stage's dword (4 blocks) of row l%16 of its row block l/16 (a 64-byte run
+  // per block), stored as [wave][block j][row][4 bytes].
   auto dma = [&](int s, int buf) {
     uint8_t* bp = BUF(buf);
     const bool live = s < nk;
@@ -916,13 +932,16 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
       buf_load_lds16(rX, bp + (wave * RP + i) * 1024, live ? xoff[i] : kBufDead, (uint32_t)s * 128);
     const int scopy = NT == 8 ? ((wave >> 1) * kBigBM + (wave & 1) * 64) : wave * 64;
     buf_load_lds4(rXs, bp + kBigBsf + scopy * 4, live ? xs_off : kBufDead, (uint32_t)s * xs_stride);
-    buf_load_lds4(rWs, bp + kBigAsf + wave * 256, live ? as_off : kBufDead, (uint32_t)(4 * s + wave) * ws_stride);
+    // stage s = 4G + u: group G at (blk * nk + 4G) * 64, row stride 4 * (stages in G), dword u
+    const uint32_t as_off = (s >> 2) < (nk >> 2) ? as_full : as_last;
+    buf_load_lds4(rWs, bp + kBigAsf + wave * 256, live ? as_off : kBufDead, (uint32_t)((s >> 2) * 256 + (s & 3) * 4));
   };
   auto compute = [&](int slot, int buf) {
     const uint8_t* bp = BUF(buf);
     int sa[4], sb[NT];
+    // weight scales: the dword of row r16 of block j holds the stage's 4 blocks; lane group g takes byte g
 #pragma unroll
-    for (int j = 0; j < 4; j++) sa[j] = bp[sa_base + sa_j[j]];
+    for (int j = 0; j < 4; j++) sa[j] = (int)(*(const uint32_t*)(bp + sa_base + j * 64) >> (8 * g));
 #pragma unroll
     for (int t = 0; t < NT; t++) sb[t] = bp[kBigBsf + (t * 16 + r16) * 4 + g];
     v4i n0 = *(const v4i*)(bp + brd0);
@@ -1004,9 +1023,10 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   const int nk = K / 128;
   const uint32_t arow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
   const uint32_t wrows = l1 ? 2u * (uint32_t)I : (uint32_t)H;
-  // the tiled weight copy: 16-row block b, K stage s at (b * nk + s) KB, in MFMA lane order
-  const uint8_t* W = l1 ? p.w1_t + (size_t)e * wrows * arow : p.w2_t + (size_t)e * wrows * arow;
-  const uint8_t* Ws = l1 ? p.w1_sf_km + (size_t)e * wrows * srow : p.w2_sf_km + (size_t)e * wrows * srow;
+  // the TILED layout: 16-row block b, K stage s at (b * nk + s) KB in MFMA lane order; its scales in
+  // groups of four stages per block
+  const uint8_t* W = l1 ? p.w1 + (size_t)e * wrows * arow : p.w2 + (size_t)e * wrows * arow;
+  const uint8_t* Ws = l1 ? p.w1_sf + (size_t)e * wrows * srow : p.w2_sf + (size_t)e * wrows * srow;
   int rb[4];  // first weight row of each 16-row block of this wave
   if (l1) {
     const int i0 = nb * 128 + wave * 32;
@@ -1025,15 +1045,15 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   // reads one 64-byte segment (the texture unit's rate is set by the number
   // of distinct segments a quad touches; row-strided operand loads touch 4)
   const uint32_t a_off = (uint32_t)lane * 16u;
-  // K-major weight scales: lane l fetches tile rows 4l..4l+3 of the wave's block
-  // (L1: gate rows of the tile for l < 32, up rows for l >= 32)
-  const uint32_t as_off = l1 ? (uint32_t)((lane < 32 ? 0 : I) + nb * 128 + 4 * (lane & 31))
-                             : (uint32_t)(nb * 256 + 4 * lane);
-  // ... and reads the byte of block g for weight row block j at sa_base + sa_j[j]
-  const uint32_t sa_base = (uint32_t)(kBigAsf + g * 256 + r16 + (l1 ? wave * 32 : wave * 64));
-  int sa_j[4];
-#pragma unroll
-  for (int j = 0; j < 4; j++) sa_j[j] = l1 ? (j >> 1) * 128 + (j & 1) * 16 : j * 16;
+  // TILED weight scales: lane l fetches row l%16 of the wave's row block l/16 (block rb[l/16] / 16):
+  // in a full group of four stages at r16 * 16, in the last group of nk % 4 stages at r16 * 4 * (nk % 4)
+  const int jl = lane >> 4;
+  const uint32_t blk_l = (uint32_t)(l1 ? (nb * 128 + wave * 32) / 16 + (jl & 1) + (jl >> 1) * (I / 16)
+                                       : (nb * 256 + wave * 64) / 16 + jl);
+  const uint32_t as_full = blk_l * (uint32_t)nk * 64u + (uint32_t)r16 * 16u;
+  const uint32_t as_last = blk_l * (uint32_t)nk * 64u + (uint32_t)r16 * 4u * (uint32_t)(nk & 3);
+  // ... and reads its row's dword of block j at sa_base + 64 j
+  const uint32_t sa_base = (uint32_t)(kBigAsf + wave * 256 + r16 * 4);
 
   // routed rows of the tile (rows past the expert repeat its first row / read
   // padding): fill instruction i of this wave covers rows 8*(RP*wave + i) + l/8
@@ -1072,7 +1092,7 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   if (NT == 8 ? wave >= 2 : wave >= 1) xs_off = kBufDead;
 
   v4f acc[4][NT];
-  big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_off, wrows, sa_base, sa_j, rX, xoff, brd0, brd1,
+  big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_full, as_last, sa_base, rX, xoff, brd0, brd1,
                 rXs, xs_off, (uint32_t)p.sg_rows * 4u, nk, wave, lane);
 
   if (!active) return;
@@ -1137,10 +1157,11 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
 #ifndef MOEFFN_W4_PP
 #define MOEFFN_W4_PP 2
 #endif
-// TILED: the weights come from the tiled copy (one contiguous 1 KB load per
-// 16-row block and K stage, already in operand order) instead of the
-// row-major matrix (two whole-line loads per block and stage pair, rebuilt by
-// the DPP shuffle).
+// TILED: the weights are in the TILED layout (one contiguous 1 KB load per
+// 16-row block and K stage, already in operand order) instead of row-major
+// (two whole-line loads per block and stage pair, rebuilt by the DPP
+// shuffle); a lane's scale load of four stages is 16 contiguous bytes in both
+// layouts (its row's dwords of a stage group).
 template <int BM, bool TILED>
 __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s, bool local, bool l1, int e, int mb,
                              int blk) {
@@ -1156,8 +1177,7 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
   const int npairs = (nk + 1) / 2;
   const uint32_t arow = (uint32_t)K / 2, srow = (uint32_t)K / 32;
   const uint32_t wrows = l1 ? 2u * (uint32_t)I : (uint32_t)H;
-  const uint8_t* W = TILED ? (l1 ? p.w1_t : p.w2_t) + (size_t)e * wrows * arow
-                           : (l1 ? p.w1 : p.w2) + (size_t)e * wrows * arow;
+  const uint8_t* W = (l1 ? p.w1 : p.w2) + (size_t)e * wrows * arow;
   const uint8_t* Ws = l1 ? p.w1_sf + (size_t)e * wrows * srow : p.w2_sf + (size_t)e * wrows * srow;
   int rb[4];
   if (l1) {
@@ -1230,8 +1250,14 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
         else
           ar[slot][j][i] = buf_load16(rW, a_voff, (uint32_t)(rb[j] + 8 * i) * arow + (uint32_t)m * 128);
       }
-      if (slot == 0)
-        sga[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rWs, as_voff, (uint32_t)rb[j] * srow + (uint32_t)m * 8, 0));
+      if (slot == 0) {
+        if constexpr (TILED)  // group of stages 2m .. 2m+3 (n of them) of 16-row block rb[j] / 16: row r16 at r16 * 4n
+          sga[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rWs, (uint32_t)r16 * 4u * (uint32_t)min(4, nk - 2 * m),
+                       ((uint32_t)(rb[j] >> 4) * (uint32_t)nk + 2u * (uint32_t)m) * 64u, 0));
+        else
+          sga[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rWs, as_voff, (uint32_t)rb[j] * srow + (uint32_t)m * 8, 0));
+      }
     }
 #pragma unroll
     for (int t = 0; t < NTB; t++) {
@@ -1372,7 +1398,7 @@ __device__ __forceinline__ void decode_tile(const Shared& sh, int E, int NB, int
 // 4/3 1,272, 3/2 1,239).
 constexpr int kWaveTileWavesL1 = 3, kWaveTileWavesL2 = 2;
 
-template <int RECIPE, int BM>
+template <int RECIPE, int BM, bool TILED>
 __device__ void phase_wave_tiles(const KParams& p, Shared& sh, const int* lr2s, bool local, bool l1) {
   const int lane = threadIdx.x & 63;
   if ((threadIdx.x >> 6) >= (l1 ? kWaveTileWavesL1 : kWaveTileWavesL2)) return;
@@ -1389,12 +1415,8 @@ __device__ void phase_wave_tiles(const KParams& p, Shared& sh, const int* lr2s, 
     int e, mb, blk;
     decode_tile(sh, E, NB, (int)t, e, mb, blk);
     if constexpr (RECIPE == 2) {
-      if (p.w1_t)
-        wave_tile_w4<BM, true>(p, sh, lr2s, local, l1, __builtin_amdgcn_readfirstlane(e),
-                               __builtin_amdgcn_readfirstlane(mb), __builtin_amdgcn_readfirstlane(blk));
-      else
-        wave_tile_w4<BM, false>(p, sh, lr2s, local, l1, __builtin_amdgcn_readfirstlane(e),
-                                __builtin_amdgcn_readfirstlane(mb), __builtin_amdgcn_readfirstlane(blk));
+      wave_tile_w4<BM, TILED>(p, sh, lr2s, local, l1, __builtin_amdgcn_readfirstlane(e),
+                              __builtin_amdgcn_readfirstlane(mb), __builtin_amdgcn_readfirstlane(blk));
     } else {
       wave_tile<RECIPE, BM>(p, sh, lr2s, local, l1, e, mb, blk);
     }
@@ -1402,7 +1424,7 @@ __device__ void phase_wave_tiles(const KParams& p, Shared& sh, const int* lr2s, 
 }
 
 // Workgroup-tile phase (token blocks of 64/128).
-template <int RECIPE, int BM>
+template <int RECIPE, int BM, bool TILED>
 __device__ void phase_wg_tiles(const KParams& p, Shared& sh, SharedB<BM>& sb, const int* lr2s, bool local, bool l1) {
   const int tid = threadIdx.x;
   const int E = p.E;
@@ -1420,7 +1442,7 @@ __device__ void phase_wg_tiles(const KParams& p, Shared& sh, SharedB<BM>& sb, co
     if (tid == 0) next = __hip_atomic_fetch_add(q, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int e, mb, nb;
     decode_tile(sh, E, NB, (int)t, e, mb, nb);
-    gemm_tile<RECIPE, BM>(p, sh, sb, lr2s, local, l1, e, mb, nb);
+    gemm_tile<RECIPE, BM, TILED>(p, sh, sb, lr2s, local, l1, e, mb, nb);
   }
 }
 
@@ -1561,10 +1583,11 @@ __device__ void phase_combine(const KParams& p) {
 // so that two workgroups fit on one CU, which keeps the grid co-resident when
 // another stream holds a few CUs of an XCD.
 // ---------------------------------------------------------------------------
-template <int RECIPE, int BM>
+template <int RECIPE, int BM, bool TILED>
 __device__ __forceinline__ void run_call(const KParams& p, Shared& sh, WaveCounters& wcnt, int* lr2s,
                                          SharedB<(BM > 32 && BM < 128 ? BM : 16)>* sb, const BigRing* big) {
   constexpr bool kBig = RECIPE == 2 && BM == kBigBM;
+  static_assert(!kBig || TILED, "the 128-row tiles read the TILED layout");
   const int tid = threadIdx.x;
   const int S = p.T * p.k;
   const bool local = !kBig && S <= kLocalRouteSlots;
@@ -1584,12 +1607,12 @@ __device__ __forceinline__ void run_call(const KParams& p, Shared& sh, WaveCount
       if (!grid_barrier(p, BAR_SCATTER, sh)) goto done;
     }
     if constexpr (kBig) phase_big_tiles<RECIPE>(p, sh, *big, true);
-    else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM>(p, sh, lr2s, local, true);
-    else phase_wg_tiles<RECIPE, BM>(p, sh, *sb, lr2s, local, true);
+    else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM, TILED>(p, sh, lr2s, local, true);
+    else phase_wg_tiles<RECIPE, BM, TILED>(p, sh, *sb, lr2s, local, true);
     if (!grid_barrier(p, BAR_L1, sh)) goto done;
     if constexpr (kBig) phase_big_tiles<RECIPE>(p, sh, *big, false);
-    else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM>(p, sh, lr2s, local, false);
-    else phase_wg_tiles<RECIPE, BM>(p, sh, *sb, lr2s, local, false);
+    else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM, TILED>(p, sh, lr2s, local, false);
+    else phase_wg_tiles<RECIPE, BM, TILED>(p, sh, *sb, lr2s, local, false);
     if (!grid_barrier(p, BAR_L2, sh)) goto done;
     phase_combine(p);
   }
@@ -1618,7 +1641,7 @@ done:
   }
 }
 
-template <int RECIPE, int BM>
+template <int RECIPE, int BM, bool TILED>
 __global__ __launch_bounds__(kThreads, 2) void moe_ffn_kernel(KParams p) {
   __shared__ Shared sh;
   if constexpr (RECIPE == 2 && BM == kBigBM) {
@@ -1629,44 +1652,43 @@ __global__ __launch_bounds__(kThreads, 2) void moe_ffn_kernel(KParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t ring2[kBigBuf];
     static_assert(sizeof(WaveCounters) <= kBigBuf, "scatter counters must fit a ring buffer");
     const BigRing R{ring0, ring1, ring2};
-    run_call<RECIPE, BM>(p, sh, *reinterpret_cast<WaveCounters*>(ring0), nullptr, nullptr, &R);
+    run_call<RECIPE, BM, TILED>(p, sh, *reinterpret_cast<WaveCounters*>(ring0), nullptr, nullptr, &R);
   } else {
     __shared__ WaveCounters wcnt;
     __shared__ int lr2s[kLocalRouteSlots];
     __shared__ SharedB<(BM > 32 && BM < 128 ? BM : 16)> sb;
-    run_call<RECIPE, BM>(p, sh, wcnt, lr2s, &sb, nullptr);
+    run_call<RECIPE, BM, TILED>(p, sh, wcnt, lr2s, &sb, nullptr);
   }
 }
 
 int max_block_m(int recipe) { return recipe == 2 ? 128 : 64; }
 
 // ---------------------------------------------------------------------------
-// Weight-scale transform: a workgroup re-orders one 64-row x 64-block tile of
-// one expert's scale matrix through LDS (row-major in, K-major out).
+// Weight-scale transform to the TILED layout: one thread per (expert, row,
+// K stage) moves the stage's dword (its four 32-block scales): row r = 16b + i,
+// stage s = 4G + u goes to (b * nk + 4G) * 64 + i * 4n + u * 4 of the expert's
+// scales, n = min(4, nk - 4G).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void transform_scales_kernel(const uint8_t* __restrict__ src,
-                                                                uint8_t* __restrict__ dst, int64_t rows, int64_t kb) {
-  __shared__ uint8_t tile[64][65];
-  const int64_t e = blockIdx.z;
-  const int64_t r0 = (int64_t)blockIdx.y * 64, b0 = (int64_t)blockIdx.x * 64;
-  const uint8_t* s = src + e * rows * kb;
-  uint8_t* d = dst + e * rows * kb;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int r = i >> 6, b = i & 63;
-    tile[r][b] = (r0 + r < rows && b0 + b < kb) ? s[(r0 + r) * kb + b0 + b] : (uint8_t)0;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
-    const int b = i >> 6, r = i & 63;
-    if (r0 + r < rows && b0 + b < kb) d[(b0 + b) * rows + r0 + r] = tile[r][b];
+__global__ __launch_bounds__(256) void transform_scales_kernel(const uint32_t* __restrict__ src,
+                                                                uint32_t* __restrict__ dst, int64_t E, int64_t rows,
+                                                                int64_t nk) {
+  const int64_t n = E * rows * nk;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < n; c += (int64_t)gridDim.x * 256) {
+    const int64_t er = c / nk, s = c - er * nk;   // er = e * rows + r
+    const int64_t e = er / rows, r = er - e * rows;
+    const int64_t b = r >> 4, i = r & 15, g4 = s & ~(int64_t)3;
+    const int64_t ns = nk - g4 < 4 ? nk - g4 : 4;
+    dst[e * rows * nk + (b * nk + g4) * 16 + i * ns + (s & 3)] = src[c];
   }
 }
 
 hipError_t launch_transform_scales(const uint8_t* src, uint8_t* dst, int64_t E, int64_t rows, int64_t kb,
                                    hipStream_t stream) {
-  if ((kb + 63) / 64 > 0x7FFFFFFF || (rows + 63) / 64 > 65535 || E > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((kb + 63) / 64), (unsigned)((rows + 63) / 64), (unsigned)E);
-  hipLaunchKernelGGL(transform_scales_kernel, grid, dim3(256), 0, stream, src, dst, rows, kb);
+  const int64_t n = E * rows * (kb / 4);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(transform_scales_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const uint32_t*>(src), reinterpret_cast<uint32_t*>(dst), E, rows, kb / 4);
   return hipGetLastError();
 }
 
@@ -1693,30 +1715,30 @@ hipError_t launch_transform_weights(const uint8_t* src, uint8_t* dst, int64_t E,
   return hipGetLastError();
 }
 
-template <int RECIPE, int BM>
+template <int RECIPE, int BM, bool TILED>
 static hipError_t launch_one(int grid, const KParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((moe_ffn_kernel<RECIPE, BM>), dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((moe_ffn_kernel<RECIPE, BM, TILED>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int RECIPE>
+template <int RECIPE, bool TILED>
 static hipError_t launch_recipe(int bm, int grid, const KParams& p, hipStream_t stream) {
   switch (bm) {
-    case 16: return launch_one<RECIPE, 16>(grid, p, stream);
-    case 32: return launch_one<RECIPE, 32>(grid, p, stream);
-    case 64: return launch_one<RECIPE, 64>(grid, p, stream);
+    case 16: return launch_one<RECIPE, 16, TILED>(grid, p, stream);
+    case 32: return launch_one<RECIPE, 32, TILED>(grid, p, stream);
+    case 64: return launch_one<RECIPE, 64, TILED>(grid, p, stream);
     case 128:
-      if constexpr (RECIPE == 2) return launch_one<RECIPE, 128>(grid, p, stream);
+      if constexpr (RECIPE == 2 && TILED) return launch_one<RECIPE, 128, TILED>(grid, p, stream);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_forward(int recipe, int bm, int grid, const KParams& p, hipStream_t stream) {
+hipError_t launch_forward(int recipe, int bm, bool tiled, int grid, const KParams& p, hipStream_t stream) {
   switch (recipe) {
-    case 0: return launch_recipe<0>(bm, grid, p, stream);
-    case 1: return launch_recipe<1>(bm, grid, p, stream);
-    case 2: return launch_recipe<2>(bm, grid, p, stream);
+    case 0: return tiled ? hipErrorInvalidValue : launch_recipe<0, false>(bm, grid, p, stream);
+    case 1: return tiled ? hipErrorInvalidValue : launch_recipe<1, false>(bm, grid, p, stream);
+    case 2: return tiled ? launch_recipe<2, true>(bm, grid, p, stream) : launch_recipe<2, false>(bm, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

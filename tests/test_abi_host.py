@@ -78,11 +78,20 @@ def test_token_alignment_and_strerror():
     ((-1, 256, 128, 8, 2, mf.RECIPE_FP8_FP4), mf.ERR_INVALID_ARG),
     ((16, 256, 128, 0, 2, mf.RECIPE_FP8_FP4), mf.ERR_INVALID_ARG),
     ((16, 256, 128, 8, 2, 3), mf.ERR_INVALID_ARG),
+    ((16, 256, 128, 8, 2, mf.RECIPE_FP8_FP4, 2), mf.ERR_INVALID_ARG),               # no such weight layout
+    ((16, 256, 128, 8, 2, mf.RECIPE_BF16, mf.WEIGHTS_TILED), mf.ERR_UNSUPPORTED),   # TILED holds e2m1 only
+    ((16, 256, 128, 8, 2, mf.RECIPE_FP8_FP8, mf.WEIGHTS_TILED), mf.ERR_UNSUPPORTED),
 ])
 def test_problem_validation(dims, code):
     with pytest.raises(mf.MoeFFNError) as ei:
         mf.get_workspace_size(mf.make_problem(*dims))
     assert ei.value.code == code
+
+
+def test_tiled_layout_problem_has_the_same_workspace():
+    a = mf.get_workspace_size(mf.make_problem(8192, 7168, 2048, 256, 8, mf.RECIPE_FP8_FP4, mf.WEIGHTS_ROW_MAJOR))
+    b = mf.get_workspace_size(mf.make_problem(8192, 7168, 2048, 256, 8, mf.RECIPE_FP8_FP4, mf.WEIGHTS_TILED))
+    assert a == b
 
 
 # Byte ranges the tiles address with 32-bit offsets must stay below 2^31:
@@ -158,13 +167,15 @@ def test_forward_rejects_small_workspace():
 @pytest.mark.parametrize("kw,code", [
     (dict(src=None), mf.ERR_INVALID_ARG),
     (dict(dst=None), mf.ERR_INVALID_ARG),
-    (dict(rows=6), mf.ERR_INVALID_ARG),        # rows not a multiple of 4
+    (dict(rows=24), mf.ERR_INVALID_ARG),       # rows not a multiple of 16
+    (dict(kb=6), mf.ERR_INVALID_ARG),          # k_blocks not a multiple of 4 (whole 128-element stages)
     (dict(kb=0), mf.ERR_INVALID_ARG),
     (dict(E=0), mf.ERR_INVALID_ARG),
     (dict(dst=4098), mf.ERR_INVALID_ARG),      # dst not 4-byte aligned
+    (dict(src=4097), mf.ERR_INVALID_ARG),      # src not 4-byte aligned
 ])
 def test_transform_weight_scales_argument_checks(kw, code):
-    a = dict(src=4096, dst=8192, E=2, rows=8, kb=3)
+    a = dict(src=4096, dst=8192, E=2, rows=16, kb=4)
     a.update(kw)
     rc = mf.lib().moe_ffn_transform_weight_scales(
         None if a["src"] is None else ctypes.c_void_p(a["src"]), None if a["dst"] is None else ctypes.c_void_p(a["dst"]),

@@ -80,39 +80,45 @@ def test_fp8xfp8_config_full():
     fp8_parity(run, p, "fp8xfp8 T512 (C2)")
 
 
-@pytest.mark.parametrize("T,E,k,prepared", [(64, 32, 8, True), (96, 32, 8, True), (40, 8, 4, True),
-                                             (333, 8, 3, True), (1000, 4, 2, True), (2048, 8, 4, True),
-                                             (64, 32, 8, False), (96, 32, 8, False), (333, 8, 3, False)])
-def test_fp8xfp4_reduced_full(T, E, k, prepared):
-    # spans token-block sizes 16..128 (average rows per expert 16 .. 1024) and ragged tails;
-    # prepared=False: no tiled weights / K-major scales (row-major loads in every tile kind)
+TILED, ROW_MAJOR = 1, 0
+
+
+@pytest.mark.parametrize("T,E,k,layout", [(64, 32, 8, TILED), (96, 32, 8, TILED), (40, 8, 4, TILED),
+                                           (333, 8, 3, TILED), (1000, 4, 2, TILED), (2048, 8, 4, TILED),
+                                           (64, 32, 8, ROW_MAJOR), (96, 32, 8, ROW_MAJOR), (333, 8, 3, ROW_MAJOR),
+                                           (2048, 8, 4, ROW_MAJOR)])
+def test_fp8xfp4_reduced_full(T, E, k, layout):
+    # spans token-block sizes 16..128 (average rows per expert 16 .. 1024) and ragged tails, with the
+    # weights in the TILED layout (every tile kind, the 128-row one included) or row-major
     cfg = _small_cfg(synth.RECIPE_FP8_FP4, T, 1024, 512, E, k, "softmax", seed=T + E)
     p = synth.make_problem(cfg, threads=8)
-    log(f"fp8xfp4 reduced T={T} E={E} k={k} prepared={prepared}")
-    run = Runner(p, kmajor=prepared)
+    log(f"fp8xfp4 reduced T={T} E={E} k={k} layout={layout}")
+    run = Runner(p, layout=layout)
     run.run()
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     _check_tables(run, p, T)
-    fp8_parity(run, p, f"fp8xfp4 T={T} E={E} k={k} prepared={prepared}")
+    fp8_parity(run, p, f"fp8xfp4 T={T} E={E} k={k} layout={layout}")
 
 
+@pytest.mark.parametrize("bm", [128, 64, 32, 16])
 @pytest.mark.parametrize("T,H,I,E,k", [
     (300, 384, 128, 4, 2),    # K stages: L1 3, L2 1 (no steady loop); odd H/128: half-empty last L2 block
-    (257, 1152, 640, 2, 1),   # L1 9 stages, L2 5 (two trailing stages); ragged last token block
+    (257, 1152, 640, 2, 1),   # L1 9 stages, L2 5 (two trailing stages; last scale groups of 1 stage); ragged
     (520, 1024, 512, 3, 3),   # several full 128-row blocks per expert
 ])
-def test_fp8xfp4_block128_shapes(T, H, I, E, k, monkeypatch):
-    monkeypatch.setenv("MOE_FFN_BLOCK_M", "128")
+def test_fp8xfp4_block128_shapes(T, H, I, E, k, bm, monkeypatch):
+    # ragged K-stage counts (partial last scale group of the TILED layout) on every tile kind
+    monkeypatch.setenv("MOE_FFN_BLOCK_M", str(bm))
     cfg = _small_cfg(synth.RECIPE_FP8_FP4, T, H, I, E, k, "softmax", seed=T + H)
     p = synth.make_problem(cfg, threads=8)
-    log(f"block 128: T={T} H={H} I={I} E={E} k={k}")
+    log(f"block {bm}: T={T} H={H} I={I} E={E} k={k}")
     run = Runner(p)
     run.run()
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     _check_tables(run, p, T)
-    fp8_parity(run, p, f"block 128 T={T} H={H} I={I}")
+    fp8_parity(run, p, f"block {bm} T={T} H={H} I={I}")
 
 
 def test_deepseek_T128_all_tokens():
@@ -219,17 +225,33 @@ def test_graph_replay_changed_inputs_matches_eager():
         fp8_parity(run, q, f"replay {r}")
 
 
-@pytest.mark.parametrize("E,rows,kb", [(3, 8, 3), (2, 256, 12), (2, 4096, 224), (1, 7168, 64)])
+def tiled_scales_reference(src: np.ndarray) -> np.ndarray:
+    """The TILED scale layout written out: per expert and 16-row block, groups of four K stages,
+    each group [16 rows][n stages][4 blocks] (n = stages left, at most 4)."""
+    E, rows, kb = src.shape
+    nk = kb // 4
+    out = np.empty(E * rows * kb, np.uint8)
+    for e in range(E):
+        for b in range(rows // 16):
+            for G in range((nk + 3) // 4):
+                n = min(4, nk - 4 * G)
+                base = e * rows * kb + (b * nk + 4 * G) * 64
+                out[base: base + 64 * n] = src[e, 16 * b: 16 * b + 16, 16 * G: 16 * G + 4 * n].reshape(-1)
+    return out
+
+
+@pytest.mark.parametrize("E,rows,kb", [(3, 16, 4), (2, 256, 12), (2, 48, 20), (1, 32, 36), (2, 4096, 224),
+                                       (1, 7168, 64)])
 def test_transform_weight_scales_bitexact(E, rows, kb):
     import mixture_experts_ffn_histogram_amd as mf
     rng = np.random.default_rng(rows + kb)
     src = rng.integers(0, 256, size=(E, rows, kb), dtype=np.uint8)
     s = torch.from_numpy(src).cuda()
-    d = torch.full((E, kb, rows), 0xA5, dtype=torch.uint8, device="cuda")
-    log(f"transform E={E} rows={rows} kb={kb}")
+    d = torch.full((E, rows, kb), 0xA5, dtype=torch.uint8, device="cuda")
+    log(f"scale transform E={E} rows={rows} kb={kb}")
     mf.transform_weight_scales(s, d, E, rows, kb)
     torch.cuda.synchronize()
-    assert np.array_equal(d.cpu().numpy(), np.ascontiguousarray(src.transpose(0, 2, 1)))
+    assert np.array_equal(d.cpu().numpy().reshape(-1), tiled_scales_reference(src))
 
 
 @pytest.mark.parametrize("E,rows,kbytes", [(3, 16, 64), (2, 48, 192), (2, 4096, 3584), (1, 7168, 1024)])
@@ -247,19 +269,19 @@ def test_transform_weights_bitexact(E, rows, kbytes):
     assert np.array_equal(d.cpu().numpy().reshape(-1), np.ascontiguousarray(ref).reshape(-1))
 
 
-def test_large_call_without_kmajor_scales_uses_64_row_tiles(monkeypatch):
-    # the 128-row tiles need the K-major weight-scale copies; without them the
-    # call runs on 64-row tiles and must give the same answer
+def test_large_call_row_major_uses_64_row_tiles(monkeypatch):
+    # the 128-row tiles read the TILED layout; a row-major call asking for them runs on 64-row
+    # tiles and must give the same answer
     monkeypatch.setenv("MOE_FFN_BLOCK_M", "128")
     cfg = _small_cfg(synth.RECIPE_FP8_FP4, 520, 1024, 512, 3, 3, "softmax", seed=5)
     p = synth.make_problem(cfg, threads=8)
-    log("block 128 requested, no K-major scales")
-    run = Runner(p, kmajor=False)
-    fp8_parity(run, p, "no K-major scales")
+    log("block 128 requested, row-major weights")
+    run = Runner(p, layout=ROW_MAJOR)
+    fp8_parity(run, p, "row-major (64-row tiles)")
     y64 = run.y.clone()
-    run_km = Runner(p)
-    fp8_parity(run_km, p, "K-major scales")
-    log(f"  64-row vs 128-row tiles: {int((y64 != run_km.y).sum())} of {y64.numel()} y elements differ in the last bit")
+    run_t = Runner(p, layout=TILED)
+    fp8_parity(run_t, p, "TILED (128-row tiles)")
+    log(f"  64-row vs 128-row tiles: {int((y64 != run_t.y).sum())} of {y64.numel()} y elements differ in the last bit")
 
 
 # Control-block words (32-bit) of the workspace: bar[0..5], exit_count 6,
