@@ -140,6 +140,19 @@ int moe_ffn_get_token_alignment(int32_t recipe, int64_t* alignment);
 int moe_ffn_forward(const moe_ffn_problem* problem, const moe_ffn_args* args,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* The forward without any allocation, for callers that cannot allocate (code
+   under HIP graph capture, tight serving loops, harnesses that forbid
+   allocation): the same computation and arguments as moe_ffn_forward, on a
+   workspace the library keeps in a static device array of
+   MOE_FFN_NOALLOC_MAX_WORKSPACE bytes per GPU (held until the process ends).
+   Problems whose moe_ffn_get_workspace_size exceeds that return
+   MOE_FFN_ERR_WORKSPACE_TOO_SMALL (e.g. the DeepSeek shape up to about 256
+   tokens fits).  Each call clears the array's control block with a kernel on
+   `stream` before the forward; calls that overlap on one GPU share the array
+   and race.  Calls no hipMalloc / hipFree; other errors as moe_ffn_forward. */
+#define MOE_FFN_NOALLOC_MAX_WORKSPACE (64u << 20)
+int moe_ffn_forward_noalloc(const moe_ffn_problem* problem, const moe_ffn_args* args, void* stream);
+
 /* Weight-scale transform to the TILED layout (the weight transform step of
    the pages' host API, done once per set of weights).  src: the row-major e8m0
    scales [num_experts, rows, k_blocks] of one weight matrix (W1: rows = 2I,

@@ -61,7 +61,8 @@ class WorkspaceView(ctypes.Structure):
 EXPORTS = ("moe_ffn_get_workspace_size", "moe_ffn_get_token_alignment", "moe_ffn_forward",
            "moe_ffn_strerror", "moe_ffn_launch_size", "moe_ffn_get_workspace_view",
            "moe_ffn_transform_weight_scales", "moe_ffn_quantize_activations", "moe_ffn_route_topk",
-           "moe_ffn_transform_weights")
+           "moe_ffn_transform_weights", "moe_ffn_forward_noalloc")
+NOALLOC_MAX_WORKSPACE = 64 << 20
 
 _lib = None
 
@@ -96,6 +97,8 @@ def lib():
         L.moe_ffn_route_topk.restype = ctypes.c_int
         L.moe_ffn_transform_weights.argtypes = [P, P, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, P]
         L.moe_ffn_transform_weights.restype = ctypes.c_int
+        L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(Problem), ctypes.POINTER(Args), P]
+        L.moe_ffn_forward_noalloc.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -215,6 +218,29 @@ def tile_weights(w1, w1_sf, w2, w2_sf, num_experts: int, hidden: int, intermedia
     return w1t, s1t, w2t, s2t
 
 
+def _args(num_tokens, x, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf, y, y_dtype, activation_clamp,
+          reserved_cus, max_cus, expert_counts, expert_offsets, row_to_slot, slot_to_row, status) -> Args:
+    return Args(int(num_tokens), _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),
+                _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf), _ptr(y), int(y_dtype), float(activation_clamp),
+                int(reserved_cus), int(max_cus), _ptr(expert_counts), _ptr(expert_offsets),
+                _ptr(row_to_slot), _ptr(slot_to_row), _ptr(status))
+
+
+def forward_noalloc(problem: Problem, *, num_tokens: int, x, x_sf, topk_idx, topk_weights,
+                    w1, w1_sf, w2, w2_sf, y, y_dtype: int, activation_clamp: float,
+                    reserved_cus: int = -1, max_cus: int = 0, expert_counts=None, expert_offsets=None,
+                    row_to_slot=None, slot_to_row=None, status=None, stream=None) -> None:
+    """Enqueue moe_ffn_forward_noalloc: the forward on the library's own static workspace (at most
+    NOALLOC_MAX_WORKSPACE bytes; calls overlapping on one GPU race)."""
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    a = _args(num_tokens, x, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf, y, y_dtype, activation_clamp,
+              reserved_cus, max_cus, expert_counts, expert_offsets, row_to_slot, slot_to_row, status)
+    _check(lib().moe_ffn_forward_noalloc(ctypes.byref(problem), ctypes.byref(a), ctypes.c_void_p(stream.cuda_stream)),
+           "moe_ffn_forward_noalloc")
+
+
 def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, topk_weights,
             w1, w1_sf, w2, w2_sf, y, y_dtype: int, activation_clamp: float,
             reserved_cus: int = -1, max_cus: int = 0, expert_counts=None, expert_offsets=None,
@@ -228,10 +254,8 @@ def forward(problem: Problem, workspace, *, num_tokens: int, x, x_sf, topk_idx, 
     import torch
     if stream is None:
         stream = torch.cuda.current_stream()
-    a = Args(int(num_tokens), _ptr(x), _ptr(x_sf), _ptr(topk_idx), _ptr(topk_weights),
-             _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf), _ptr(y), int(y_dtype), float(activation_clamp),
-             int(reserved_cus), int(max_cus), _ptr(expert_counts), _ptr(expert_offsets),
-             _ptr(row_to_slot), _ptr(slot_to_row), _ptr(status))
+    a = _args(num_tokens, x, x_sf, topk_idx, topk_weights, w1, w1_sf, w2, w2_sf, y, y_dtype, activation_clamp,
+              reserved_cus, max_cus, expert_counts, expert_offsets, row_to_slot, slot_to_row, status)
     rc = lib().moe_ffn_forward(ctypes.byref(problem), ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                ctypes.c_size_t(workspace.numel() * workspace.element_size()),
                                ctypes.c_void_p(stream.cuda_stream))

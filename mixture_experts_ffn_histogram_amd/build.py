@@ -20,7 +20,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 def build(verbose: bool = False, resource_usage: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     objs = []
-    for src in ("moe_ffn_kernel.hip", "moe_ffn_quant.hip", "moe_ffn_router.hip", "moe_ffn_api.cpp"):
+    for src in ("moe_ffn_kernel.hip", "moe_ffn_quant.hip", "moe_ffn_router.hip", "moe_ffn_noalloc.hip",
+                "moe_ffn_api.cpp"):
         obj = os.path.join(BUILD, src + ".o")
         cmd = [HIPCC] + COMMON + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
         if resource_usage and src.endswith(".hip"):

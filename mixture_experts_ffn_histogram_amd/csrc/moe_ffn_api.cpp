@@ -190,6 +190,15 @@ const char* moe_ffn_strerror(int code) {
 
 int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* workspace, size_t workspace_bytes,
                     void* stream) {
+  return moeffn::forward_enqueue(p, a, workspace, workspace_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+}  // extern "C"
+
+namespace moeffn {
+
+int forward_enqueue(const moe_ffn_problem* p, const moe_ffn_args* a, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream, hipError_t (*before_launch)(void* workspace, hipStream_t stream)) {
   int rc = check_problem(p);
   if (rc) return rc;
   if (!a || !workspace) return MOE_FFN_ERR_INVALID_ARG;
@@ -270,8 +279,9 @@ int moe_ffn_forward(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
     k.hsg = reinterpret_cast<uint32_t*>(ws + L.hsg);
     k.sg_rows = (int32_t)L.h_rows;
   }
-  const hipError_t err = moeffn::launch_forward(recipe, bm, tiled, grid, k, static_cast<hipStream_t>(stream));
+  if (before_launch && before_launch(workspace, stream) != hipSuccess) return MOE_FFN_ERR_HIP;
+  const hipError_t err = moeffn::launch_forward(recipe, bm, tiled, grid, k, stream);
   return err == hipSuccess ? MOE_FFN_OK : MOE_FFN_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace moeffn

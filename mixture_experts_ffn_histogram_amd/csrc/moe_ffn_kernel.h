@@ -4,9 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/moe_ffn.h"
 #include "moe_ffn_layout.h"
 
 namespace moeffn {
+
+// The forward of both entry points: checks the problem and the arguments,
+// sizes the grid and launches the persistent kernel on `workspace`.
+// `before_launch` (optional) is enqueued on the stream right before the
+// kernel, after every check passed.  Returns a MOE_FFN_* code.
+int forward_enqueue(const moe_ffn_problem* p, const moe_ffn_args* a, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream, hipError_t (*before_launch)(void* workspace, hipStream_t stream));
 
 struct KParams {
   // problem of this call

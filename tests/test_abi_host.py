@@ -236,3 +236,16 @@ def test_transform_weights_argument_checks(kw, code):
     p = lambda v: None if v is None else ctypes.c_void_p(v)
     rc = mf.lib().moe_ffn_transform_weights(p(a["src"]), p(a["dst"]), a["E"], a["rows"], a["kb"], None)
     assert rc == code
+
+
+def test_forward_noalloc_rejects_problems_beyond_its_scratch():
+    # checked before any device work: the DeepSeek shape at 8192 tokens needs ~2 GB
+    prob = mf.make_problem(8192, 7168, 2048, 256, 8, mf.RECIPE_FP8_FP4, mf.WEIGHTS_TILED)
+    assert mf.get_workspace_size(prob) > mf.NOALLOC_MAX_WORKSPACE
+    rc = mf.lib().moe_ffn_forward_noalloc(ctypes.byref(prob), ctypes.byref(_args()), None)
+    assert rc == mf.ERR_WORKSPACE_TOO_SMALL
+    # the DeepSeek shape at 128 tokens fits
+    small = mf.make_problem(128, 7168, 2048, 256, 8, mf.RECIPE_FP8_FP4, mf.WEIGHTS_TILED)
+    assert mf.get_workspace_size(small) <= mf.NOALLOC_MAX_WORKSPACE
+    bad = mf.make_problem(16, 256, 128, 0, 2, mf.RECIPE_FP8_FP4)
+    assert mf.lib().moe_ffn_forward_noalloc(ctypes.byref(bad), ctypes.byref(_args()), None) == mf.ERR_INVALID_ARG
