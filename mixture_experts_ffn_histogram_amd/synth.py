@@ -15,6 +15,9 @@ Recipe (what each tensor looks like):
     drawn with probabilities FP4_MAG_PROBS, uniform sign; scale byte per
     block 127 + round(log2(sigma / FP4_STD)) + j, j as for e4m3.
   * bf16 tensors: bf16 cast of N(0, sigma^2).
+  * the (1, 128, 128) recipe: e4m3 codes as above; one fp32 scale per
+    1 x 128 activation block, 2^u / 64 (u uniform in [-1, 1]), and per
+    128 x 128 weight block, sigma / 64 * 2^u (u uniform in [-1/2, 1/2]).
   * x of a config with x_bf16 set (the FP8 x FP8 workload): bf16 N(0, 1),
     quantised on the fly by the pre-dispatch quantiser (e4m3 + e8m0 1x32).
   * routing "softmax": logits N(0,1) [T,E] -> softmax -> top-k (descending)
@@ -37,7 +40,9 @@ import torch
 RECIPE_BF16 = 0
 RECIPE_FP8_FP8 = 1
 RECIPE_FP8_FP4 = 2
-RECIPE_NAMES = {RECIPE_BF16: "bf16", RECIPE_FP8_FP8: "fp8xfp8", RECIPE_FP8_FP4: "fp8xfp4"}
+RECIPE_FP8_B128 = 3
+RECIPE_NAMES = {RECIPE_BF16: "bf16", RECIPE_FP8_FP8: "fp8xfp8", RECIPE_FP8_FP4: "fp8xfp4",
+                RECIPE_FP8_B128: "fp8_block128"}
 
 # Probability of each E2M1 magnitude index (0, .5, 1, 1.5, 2, 3, 4, 6).
 FP4_MAG_PROBS = np.array([0.10, 0.19, 0.18, 0.16, 0.13, 0.15, 0.07, 0.02])
@@ -141,6 +146,9 @@ def _weights(cfg: Config, which: str, rows: int, K: int, threads: int):
     if cfg.recipe == RECIPE_BF16:
         w = np.empty((E, rows, K), np.uint16)
         sf = None
+    elif cfg.recipe == RECIPE_FP8_B128:
+        w = np.empty((E, rows, K), np.uint8)
+        sf = np.empty((E, rows // 128, K // 128), np.float32)
     elif cfg.recipe == RECIPE_FP8_FP8:
         w = np.empty((E, rows, K), np.uint8)
         sf = np.empty((E, rows, K // 32), np.uint8)
@@ -154,7 +162,10 @@ def _weights(cfg: Config, which: str, rows: int, K: int, threads: int):
             w[e] = _bf16_bits(rng, (rows, K), sigma)
             return
         rs = _rng(cfg.seed, tid_sf, e)
-        if cfg.recipe == RECIPE_FP8_FP8:
+        if cfg.recipe == RECIPE_FP8_B128:
+            w[e] = _e4m3_codes(rng, (rows, K))
+            sf[e] = (sigma / 64.0 * np.exp2(rs.uniform(-0.5, 0.5, size=(rows // 128, K // 128)))).astype(np.float32)
+        elif cfg.recipe == RECIPE_FP8_FP8:
             w[e] = _e4m3_codes(rng, (rows, K))
             sf[e] = _scale_bytes(rs, (rows, K // 32), int(round(math.log2(sigma / 64.0))))
         else:
@@ -218,6 +229,9 @@ def activations(cfg: Config, T: int | None = None):
     if cfg.x_bf16:
         return None, None
     x = _e4m3_codes(rng, (T, H))
+    if cfg.recipe == RECIPE_FP8_B128:
+        u = _rng(cfg.seed, _TID["x_sf"], T).uniform(-1.0, 1.0, size=(T, H // 128))
+        return x, (np.exp2(u) / 64.0).astype(np.float32)
     x_sf = _scale_bytes(_rng(cfg.seed, _TID["x_sf"], T), (T, H // 32), int(round(math.log2(1.0 / 64.0))))
     return x, x_sf
 

@@ -26,6 +26,7 @@ _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 RECIPE_BF16 = 0
 RECIPE_FP8_FP8 = 1
 RECIPE_FP8_FP4 = 2
+RECIPE_FP8_B128 = 3   # e4m3 x e4m3, fp32 scales per 1 x 128 (activations) and 128 x 128 (weights)
 
 OK = 0
 BAD_EXPERT_INDEX = 1
@@ -233,6 +234,8 @@ def ffn_row(p: dict, t: int, e: int, clamp: float, rho: float = 0.0):
                               float(rho), _ptr(delta))
     if rc < 0:
         raise RuntimeError(f"oracle_ffn_row failed: {rc}")
+    if recipe == RECIPE_FP8_B128:   # one fp32 scale per 1 x 128 block
+        hsf = hsf.view(np.float32)
     return {"c": c, "h": h, "hq": hq, "h_codes": codes, "h_sf": hsf, "o": o, "delta": delta}
 
 

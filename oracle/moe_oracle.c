@@ -17,7 +17,9 @@
  *   digest: y sliced to num_tokens; DeepGEMM PR #451: the combine step).
  *   Block-scale recipe (1, 1, 32): one e8m0 scale per 1 x 32 block along
  *   the contraction dimension for both operands (PR #36657 digest, recipe
- *   argument).
+ *   argument).  Recipe (1, 128, 128) with float scale factors (SM90 MegaMoE
+ *   dev log, Phase-1 entry): e4m3 operands, one fp32 scale per 1 x 128
+ *   activation block and per 128 x 128 weight block.
  *
  * All reductions run in double in ascending index order; every intermediate
  * that the method stores in a narrow type is rounded exactly once to it.
@@ -25,6 +27,7 @@
  * order, where the top-k weight is applied, output precision) are listed in
  * the header comment of each function below.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -36,6 +39,7 @@
 #define OR_RECIPE_BF16 0
 #define OR_RECIPE_FP8_FP8 1
 #define OR_RECIPE_FP8_FP4 2
+#define OR_RECIPE_FP8_B128 3   /* e4m3 x e4m3 with fp32 scales: 1 x 128 (activations), 128 x 128 (weights) */
 
 #define OR_OK 0
 #define OR_BAD_ARG -1
@@ -179,12 +183,17 @@ float oracle_swiglu(float gate, float up, float clamp) {
 /* O1 applied to whole rows: dequantised operand values in double.           */
 /* ------------------------------------------------------------------------ */
 
-/* Activation row (x or the re-quantised h): K values. */
+/* Activation row (x or the re-quantised h): K values.  The (1, 128, 128)
+   recipe scales each 1 x 128 block of a row by one fp32 factor, sf[row][k/128]. */
 static void dequant_act_row(int recipe, const void* base, const uint8_t* sf, int64_t row, int64_t K, double* out) {
     int64_t k;
     if (recipe == OR_RECIPE_BF16) {
         const uint16_t* p = (const uint16_t*)base + row * K;
         for (k = 0; k < K; k++) out[k] = oracle_dec_bf16(p[k]);
+    } else if (recipe == OR_RECIPE_FP8_B128) {
+        const uint8_t* p = (const uint8_t*)base + row * K;
+        const float* s = (const float*)(const void*)sf + row * (K / 128);
+        for (k = 0; k < K; k++) out[k] = oracle_dec_e4m3(p[k]) * (double)s[k / 128];
     } else {
         const uint8_t* p = (const uint8_t*)base + row * K;
         const uint8_t* s = sf + row * (K / 32);
@@ -192,12 +201,18 @@ static void dequant_act_row(int recipe, const void* base, const uint8_t* sf, int
     }
 }
 
-/* Weight row `row` of a [rows, K] matrix (rows of all experts stacked). */
+/* Weight row `row` of a [rows, K] matrix (rows of all experts stacked).  The
+   (1, 128, 128) recipe scales each 128 x 128 block by one fp32 factor,
+   sf[row / 128][k / 128] (every expert's row count is a multiple of 128). */
 static void dequant_weight_row(int recipe, const void* base, const uint8_t* sf, int64_t row, int64_t K, double* out) {
     int64_t k;
     if (recipe == OR_RECIPE_BF16) {
         const uint16_t* p = (const uint16_t*)base + row * K;
         for (k = 0; k < K; k++) out[k] = oracle_dec_bf16(p[k]);
+    } else if (recipe == OR_RECIPE_FP8_B128) {
+        const uint8_t* p = (const uint8_t*)base + row * K;
+        const float* s = (const float*)(const void*)sf + (row / 128) * (K / 128);
+        for (k = 0; k < K; k++) out[k] = oracle_dec_e4m3(p[k]) * (double)s[k / 128];
     } else if (recipe == OR_RECIPE_FP8_FP8) {
         const uint8_t* p = (const uint8_t*)base + row * K;
         const uint8_t* s = sf + row * (K / 32);
@@ -267,6 +282,60 @@ static double e4m3_spacing_at(double v, int E) {   /* grid spacing at |v| for bl
     return ldexp(e4m3_spacing(q > 448.0 ? 448.0 : q), E);
 }
 
+/* O5 of the (1, 128, 128) recipe (a reading: the pages name the recipe and its
+   float scale factors, not the quantiser): per 1 x 128 block of h,
+   s = max(fp32(amax / 448), 2^-126), code = E4M3FN code of the IEEE fp32
+   quotient fp32(h / s), rounded to nearest even and saturating; the value is
+   code * s.  (Rounding the double quotient to fp32 gives the correctly
+   rounded fp32 quotient: double has more than twice fp32's precision.) */
+static float b128_scale(double amax) {
+    float sc = (float)(amax / 448.0);
+    return sc < FLT_MIN ? FLT_MIN : sc;
+}
+
+static double b128_quotient(float h, float sc) { return (double)(float)((double)h / (double)sc); }
+
+/* The band of the (1, 128, 128) recipe (same activation band as requant_band):
+   the block's scale follows its amax continuously, so within the band it can
+   move from s_lo = scale(amax - bmax) to s_hi = scale(amax + bmax), changing
+   every value of the block by up to (|q| + spacing) * (s_hi - s_lo); an
+   element whose quotient lies within band / s_lo + |q| (s_hi - s_lo) / s_lo
+   of a rounding midpoint may also take the other code, adding band + one
+   spacing at s_hi. */
+static void requant_band_b128(const float* h, const double* band, int64_t I, double* delta) {
+    int64_t b, i;
+    for (b = 0; b < I / 128; b++) {
+        double amax = 0.0, bmax = 0.0;
+        for (i = 128 * b; i < 128 * b + 128; i++) {
+            if (band[i] > bmax) bmax = band[i];
+            if (fabs((double)h[i]) > amax) amax = fabs((double)h[i]);
+        }
+        const double sc = b128_scale(amax), s_lo = b128_scale(amax - bmax > 0.0 ? amax - bmax : 0.0);
+        const double s_hi = b128_scale(amax + bmax);
+        for (i = 128 * b; i < 128 * b + 128; i++) {
+            double q = (double)h[i] / sc;
+            double sp = e4m3_spacing(fabs(q) > 448.0 ? 448.0 : q);
+            double lo = floor(q / sp) * sp, mid = lo + 0.5 * sp;
+            double eq = band[i] / s_lo + fabs(q) * (s_hi - s_lo) / s_lo;
+            double sp_hi = e4m3_spacing(fmin(448.0, fabs(q) + eq));
+            delta[i] = (fabs(q) + sp) * (s_hi - s_lo);
+            if (fabs(q - mid) <= eq || fabs(q) + eq > 448.0) delta[i] += band[i] + sp_hi * s_hi;
+        }
+    }
+}
+
+/* Activation band of every element (see above), into band[I]. */
+static void activation_band(const float* c, const double* eps, int64_t I, float clamp, double* band) {
+    int64_t i;
+    double cc = clamp;
+    int clamp_on = isfinite(cc) && cc > 0.0;
+    for (i = 0; i < I; i++) {
+        double g = c[i], u = c[I + i], eg = eps[i], eu = eps[I + i];
+        if (clamp_on) { g = fmin(fmax(g, -cc), cc); u = fmin(fmax(u, -cc), cc); }
+        band[i] = 1.1 * eg * (fabs(u) + eu) + fabs(g / (1.0 + exp(-g))) * eu;
+    }
+}
+
 static void requant_band(const float* h, const float* c, const double* eps, int64_t I, float clamp, double* delta) {
     int64_t b, i;
     double cc = clamp;
@@ -334,7 +403,8 @@ static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
                 if (a > m) m = a;
                 if (k % 128 == 127 || k == H - 1) { S += m; m = 0.0; }
             }
-            eps[n] = rho * S + (double)steps * ldexp(A, -24);
+            /* fp32 step sums; the (1, 128, 128) recipe rounds once more (its fp32 scale product) */
+            eps[n] = rho * S + (double)steps * (p->recipe == OR_RECIPE_FP8_B128 ? 2.0 : 1.0) * ldexp(A, -24);
         }
     }
     /* O4: rows [0, I) of W1 are the gate, rows [I, 2I) the up projection. */
@@ -344,6 +414,20 @@ static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
         for (i = 0; i < I; i++) {
             hq[i] = oracle_round_bf16((double)h[i]);
             if (hq_codes) ((uint16_t*)hq_codes)[i] = oracle_enc_bf16(hq[i]);
+        }
+    } else if (p->recipe == OR_RECIPE_FP8_B128) {
+        for (b = 0; b < I / 128; b++) {
+            double amax = 0.0;
+            float sc;
+            for (i = 128 * b; i < 128 * b + 128; i++)
+                if (fabs((double)h[i]) > amax) amax = fabs((double)h[i]);
+            sc = b128_scale(amax);
+            if (hq_sf) ((float*)(void*)hq_sf)[b] = sc;
+            for (i = 128 * b; i < 128 * b + 128; i++) {
+                double q = oracle_round_e4m3_sat(b128_quotient(h[i], sc));
+                if (hq_codes) ((uint8_t*)hq_codes)[i] = oracle_enc_e4m3(q);
+                hq[i] = q * (double)sc;
+            }
         }
     } else {
         for (b = 0; b < I / 32; b++) {
@@ -365,9 +449,14 @@ static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
     {
         double* delta = NULL;
         if (want_band) {
-            delta = (double*)calloc((size_t)I, sizeof(double));
+            delta = (double*)calloc((size_t)(2 * I), sizeof(double));
             if (!delta) { free(xd); free(wd); free(c); free(h); free(hq); free(eps); return OR_NO_MEMORY; }
-            requant_band(h, c, eps, I, p->activation_clamp, delta);
+            if (p->recipe == OR_RECIPE_FP8_B128) {
+                activation_band(c, eps, I, p->activation_clamp, delta + I);
+                requant_band_b128(h, delta + I, I, delta);
+            } else {
+                requant_band(h, c, eps, I, p->activation_clamp, delta);
+            }
         }
         for (n = 0; n < H; n++) {
             dequant_weight_row(p->recipe, w2, w2_sf, e * H + n, I, wd);
@@ -455,7 +544,8 @@ static int check_inputs(const oracle_problem* p, const void* x, const uint8_t* x
 static int check_problem(const oracle_problem* p) {
     if (!p) return OR_BAD_ARG;
     if (p->num_tokens < 0 || p->hidden <= 0 || p->intermediate <= 0 || p->num_experts <= 0 || p->top_k <= 0) return OR_BAD_ARG;
-    if (p->recipe < 0 || p->recipe > 2) return OR_BAD_ARG;
+    if (p->recipe < 0 || p->recipe > 3) return OR_BAD_ARG;
+    if (p->recipe == OR_RECIPE_FP8_B128 && (p->hidden % 128 || p->intermediate % 128)) return OR_BAD_ARG;
     if (p->hidden % 32 || p->intermediate % 32) return OR_BAD_ARG;
     return OR_OK;
 }

@@ -202,6 +202,8 @@ def _torch_dequant_act(p, t):
     if p["recipe"] == synth.RECIPE_BF16:
         return [Fraction(float(v)) for v in torch.from_numpy(p["x"][t].view(np.int16)).view(torch.bfloat16).double()]
     vals = torch.from_numpy(p["x"][t]).view(torch.float8_e4m3fn).double().numpy()
+    if p["recipe"] == synth.RECIPE_FP8_B128:   # one fp32 factor per 1 x 128 block
+        return [Fraction(float(vals[h])) * Fraction(float(p["x_sf"][t, h // 128])) for h in range(H)]
     sc = torch.from_numpy(p["x_sf"][t]).view(torch.float8_e8m0fnu).double().numpy()
     return [Fraction(float(vals[h])) * Fraction(float(sc[h // 32])) for h in range(H)]
 
@@ -210,6 +212,9 @@ def _torch_dequant_w(p, which, e, n):
     w, sf = p[which], p[which + "_sf"]
     if p["recipe"] == synth.RECIPE_BF16:
         return [Fraction(float(v)) for v in torch.from_numpy(w[e, n].view(np.int16)).view(torch.bfloat16).double()]
+    if p["recipe"] == synth.RECIPE_FP8_B128:   # one fp32 factor per 128 x 128 block
+        vals = torch.from_numpy(w[e, n]).view(torch.float8_e4m3fn).double().numpy()
+        return [Fraction(float(vals[kk])) * Fraction(float(sf[e, n // 128, kk // 128])) for kk in range(len(vals))]
     sc = torch.from_numpy(sf[e, n]).view(torch.float8_e8m0fnu).double().numpy()
     if p["recipe"] == synth.RECIPE_FP8_FP8:
         vals = torch.from_numpy(w[e, n]).view(torch.float8_e4m3fn).double().numpy()
@@ -221,9 +226,11 @@ def _torch_dequant_w(p, which, e, n):
     return [Fraction(float(vals[kk])) * Fraction(float(sc[kk // 32])) for kk in range(len(vals))]
 
 
-@pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4])
+@pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4,
+                                    synth.RECIPE_FP8_B128])
 def test_gemms_exact_rationals(recipe):
-    cfg = synth.Config("tiny", recipe, 3, 64, 32, 3, 2, "uniform", 11)
+    b128 = recipe == synth.RECIPE_FP8_B128   # (its double sums round; the fp32 results still match)
+    cfg = synth.Config("tiny", recipe, 3, 256 if b128 else 64, 128 if b128 else 32, 3, 2, "uniform", 11)
     p = synth.make_problem(cfg, threads=1)
     t, e = 1, int(p["topk_idx"][1, 0])
     row = oracle.ffn_row(p, t, e, 7.0)
@@ -318,6 +325,13 @@ def _dense_ffn_torch(p, t, clamp):
     h = (torch.nn.functional.silu(g) * u).float()
     if p["recipe"] == synth.RECIPE_BF16:
         hq = h.to(torch.bfloat16).double()
+    elif p["recipe"] == synth.RECIPE_FP8_B128:
+        hq = torch.empty_like(h, dtype=torch.float64)
+        for b in range(p["I"] // 128):
+            blk = h[128 * b:128 * b + 128]
+            sc = torch.clamp(blk.abs().max() / torch.tensor(448.0), min=torch.finfo(torch.float32).tiny)  # fp32
+            q = (blk / sc).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).double()
+            hq[128 * b:128 * b + 128] = q * sc.double()
     else:
         hq = torch.empty_like(h, dtype=torch.float64)
         for b in range(p["I"] // 32):
@@ -334,9 +348,11 @@ def _dense_ffn_torch(p, t, clamp):
 
 @pytest.mark.parametrize("recipe,k,w", [(synth.RECIPE_FP8_FP4, 2, (0.25, 0.75)),
                                         (synth.RECIPE_FP8_FP8, 8, (0.125,) * 8),
-                                        (synth.RECIPE_BF16, 2, (0.5, 0.5))])
+                                        (synth.RECIPE_BF16, 2, (0.5, 0.5)),
+                                        (synth.RECIPE_FP8_B128, 2, (0.75, 0.25))])
 def test_identical_experts_reduce_to_dense_ffn(recipe, k, w):
-    cfg = synth.Config("dense", recipe, 3, 64, 64, 4 if k == 2 else 9, k, "uniform", 21)
+    dim = 256 if recipe == synth.RECIPE_FP8_B128 else 64
+    cfg = synth.Config("dense", recipe, 3, dim, dim, 4 if k == 2 else 9, k, "uniform", 21)
     p = _identical_experts(synth.make_problem(cfg, threads=1))
     p["topk_weights"] = np.tile(np.array(w, np.float32), (p["T"], 1))
     for clamp in (7.0, 0.0):
@@ -353,11 +369,13 @@ def test_identical_experts_reduce_to_dense_ffn(recipe, k, w):
 # whole forward: invariants
 # --------------------------------------------------------------------------
 def _small(recipe, routing="softmax", T=24, seed=5):
-    cfg = synth.Config("small", recipe, T, 64, 64, 6, 3, routing, seed)
+    dim = 128 if recipe == synth.RECIPE_FP8_B128 else 64
+    cfg = synth.Config("small", recipe, T, dim, dim, 6, 3, routing, seed)
     return synth.make_problem(cfg, threads=1)
 
 
-@pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4])
+@pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4,
+                                    synth.RECIPE_FP8_B128])
 def test_empty_experts_contribute_nothing(recipe):
     p = _small(recipe)
     used = set(p["topk_idx"].ravel().tolist())
@@ -375,13 +393,13 @@ def test_empty_experts_contribute_nothing(recipe):
             s = p[n + "_sf"].copy()
             for e in range(p["E"]):
                 if e not in used:
-                    s[e] = 0xFF                                           # e8m0 NaN
+                    s[e] = np.nan if s.dtype == np.float32 else 0xFF      # fp32 / e8m0 NaN
             q[n + "_sf"] = s
     got = oracle.forward(q, True, 7.0)["y"]
     assert np.all(np.isfinite(got)) and np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("recipe", [synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4])
+@pytest.mark.parametrize("recipe", [synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4, synth.RECIPE_FP8_B128])
 def test_token_permutation_permutes_output(recipe):
     p = _small(recipe)
     perm = np.random.default_rng(9).permutation(p["T"])
@@ -393,7 +411,7 @@ def test_token_permutation_permutes_output(recipe):
     assert np.array_equal(a[perm], b)
 
 
-@pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP4])
+@pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP4, synth.RECIPE_FP8_B128])
 def test_per_token_path_equals_routed_path(recipe):
     p = _small(recipe, T=20)
     p["topk_idx"][3, 1] = -1
@@ -480,3 +498,62 @@ def test_forward_tokens_rows_hands_back_each_slots_row():
             row = oracle.ffn_row(p, t, e, 7.0, rho=2.0 ** -8)
             assert np.array_equal(hq[q, j], row["hq"]) and np.array_equal(delta[q, j], row["delta"])
     assert np.nanmax(delta) > 0.0
+
+
+# --------------------------------------------------------------------------
+# the (1, 128, 128) recipe with fp32 scale factors
+# --------------------------------------------------------------------------
+def test_block128_requant_rule():
+    # per 1 x 128 block: s = max(fp32(amax / 448), smallest normal fp32); codes = torch's e4m3 cast of the
+    # IEEE fp32 quotient h / s; the block max lands on 448; values = code * s
+    cfg = synth.Config("b128", synth.RECIPE_FP8_B128, 6, 256, 384, 4, 2, "softmax", 17)
+    p = synth.make_problem(cfg, threads=1)
+    for t, j in ((0, 0), (3, 1), (5, 0)):
+        row = oracle.ffn_row(p, t, int(p["topk_idx"][t, j]), 7.0)
+        h = torch.from_numpy(row["h"])                         # fp32
+        codes = torch.from_numpy(row["h_codes"]).view(torch.float8_e4m3fn)
+        for b in range(p["I"] // 128):
+            blk = h[128 * b:128 * b + 128]
+            sc = torch.clamp(blk.abs().max() / torch.tensor(448.0), min=torch.finfo(torch.float32).tiny)
+            assert row["h_sf"][b] == sc.item()
+            ref = (blk / sc).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+            assert torch.equal(ref.view(torch.uint8), codes[128 * b:128 * b + 128].view(torch.uint8))
+            cb = codes[128 * b:128 * b + 128].double()
+            assert cb.abs().max().item() == 448.0
+            assert np.array_equal(row["hq"][128 * b:128 * b + 128], (cb * float(sc)).numpy())
+
+
+def _closed_form_b128_problem():
+    # T=1, H=I=128, E=2, k=2: x codes 1.0 with scale 0.5; W1 gate codes 0.5 (scale 3.0), up codes -1.0
+    # (scale 0.25); W2 codes 1.0 (expert 0) / 2.0 (expert 1), scale 0.5; weights 0.25, 0.75
+    T, H, I, E, k = 1, 128, 128, 2, 2
+    p = {"name": "closed_b128", "T": T, "H": H, "I": I, "E": E, "k": k, "recipe": synth.RECIPE_FP8_B128}
+    p["x"] = np.full((T, H), 0x38, np.uint8)
+    p["x_sf"] = np.full((T, 1), 0.5, np.float32)
+    w1 = np.zeros((E, 2 * I, H), np.uint8)
+    w1[:, :I] = 0x30      # e4m3 0.5
+    w1[:, I:] = 0xB8      # e4m3 -1.0
+    s1 = np.zeros((E, 2, 1), np.float32)
+    s1[:, 0] = 3.0
+    s1[:, 1] = 0.25
+    p["w1"], p["w1_sf"] = w1, s1
+    w2 = np.zeros((E, H, I), np.uint8)
+    w2[0] = 0x38          # 1.0
+    w2[1] = 0x40          # 2.0
+    p["w2"], p["w2_sf"] = w2, np.full((E, 1, 1), 0.5, np.float32)
+    p["topk_idx"] = np.array([[0, 1]], np.int32)
+    p["topk_weights"] = np.array([[0.25, 0.75]], np.float32)
+    return p
+
+
+@pytest.mark.parametrize("case,clamp", [("clamp7", 7.0), ("no_clamp", 0.0)])
+def test_closed_form_block128_example(case, clamp):
+    gold = json.load(open(os.path.join(GOLDEN, "closed_form_block128.json")))["expected"][case]
+    p = _closed_form_b128_problem()
+    out = oracle.forward(p, y_fp32=True, clamp=clamp)
+    assert np.all(out["y"][0] == gold["y"])
+    row = oracle.ffn_row(p, 0, 1, clamp)
+    assert np.all(row["h"] == np.float32(gold["h"]))
+    assert row["h_sf"][0] == np.float32(gold["h_sf"])
+    assert np.all(row["h_codes"] == gold["h_code"])
+    assert np.all(row["o"] == np.float32(gold["o_expert1"]))
