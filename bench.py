@@ -52,8 +52,11 @@ def algorithmic_bytes(p, active_experts: int) -> int:
     """Bytes one call must move at least: the weights (+scales) of every expert
     that receives a token, x (+scales), topk, and y (bf16)."""
     H, I, T, k = p["H"], p["I"], p["T"], p["k"]
-    per_expert = 2 * I * (H // 2) + 2 * I * (H // 32) + H * (I // 2) + H * (I // 32)
-    per_token = H + H // 32 + k * 8 + H * 2
+    w = {0: 2.0, 1: 1.0, 2: 0.5, 3: 1.0}[p["recipe"]]                  # weight bytes per element
+    sf = {0: 0.0, 1: 1 / 32, 2: 1 / 32, 3: 4 / (128 * 128)}[p["recipe"]]  # weight scale bytes per element
+    xe = {0: 2.0, 1: 1.0, 2: 1.0, 3: 1.0}[p["recipe"]] + {0: 0.0, 1: 1 / 32, 2: 1 / 32, 3: 4 / 128}[p["recipe"]]
+    per_expert = int(3 * I * H * (w + sf))
+    per_token = int(H * xe) + k * 8 + H * 2
     return active_experts * per_expert + T * per_token
 
 
@@ -436,6 +439,18 @@ def main() -> int:
         log(f"[bench] C2: {ms2 * 1e3:.1f} us/call quantise + forward, {ms2f * 1e3:.1f} forward, "
             f"{gb2:.0f} GB/s")
         c2.free()
+        # the (1, 128, 128) recipe with fp32 scales at the same shape (two weight copies in turn)
+        b8 = Workload("fp8block128_T512_H2048_I768_E64_k6", args.threads, log, weight_copies=2)
+        msb = b8.time(100, 10)
+        gbb = b8.bytes / (msb * 1e-3) / 1e9
+        out["block128_fp32_scales_T512"] = {
+            "workload": "fp8block128_T512_H2048_I768_E64_k6", "us_per_call": round(msb * 1e3, 2),
+            "useful_tflops": round(b8.flops / (msb * 1e-3) / 1e12, 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbb, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbb / PEAK_HBM_GBS, 4), "work_per_launch": f"{b8.bytes} algorithmic bytes"},
+            "weights": "2 copies used in turn (not cache-resident)"}
+        log(f"[bench] (1,128,128) T=512: {msb * 1e3:.1f} us/call, {gbb:.0f} GB/s")
+        b8.free()
     if not args.no_quantize:
         out["quantize"] = run_quantize(p["T"], p["H"], args.steps, args.warmup, log)
         out["router"] = run_router(p["T"], p["H"], p["E"], p["k"], args.steps, args.warmup, log)

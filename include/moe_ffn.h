@@ -45,6 +45,14 @@ extern "C" {
 #define MOE_FFN_RECIPE_BF16 0     /* x, W1, W2 bf16; no scales; h re-rounded to bf16       */
 #define MOE_FFN_RECIPE_FP8_FP8 1  /* x, W e4m3 + e8m0 per 1x32 along K; h e4m3 + e8m0     */
 #define MOE_FFN_RECIPE_FP8_FP4 2  /* x e4m3, W e2m1 (packed), e8m0 per 1x32 along K       */
+/* Recipe (1, 128, 128) with float scale factors ("SM90 MegaMoE dev log",
+   Phase-1 entry: the wrapper's recipe (1, 128, 128) with the float SF path):
+   x, W e4m3; one fp32 scale per 1 x 128 block of an activation row and per
+   128 x 128 block of a weight matrix; h re-quantised per 1 x 128 block with
+   s = max(fp32(amax / 448), 2^-126) and code = e4m3 (nearest even,
+   saturating) of the IEEE fp32 quotient h / s.  H and I multiples of 128;
+   runs on 64-row token blocks; row-major weights only. */
+#define MOE_FFN_RECIPE_FP8_BLOCK128 3
 
 /* Storage layout of the weights (moe_ffn_problem.weight_layout):
    ROW_MAJOR: w1 [E, 2I, H] and w2 [E, H, I] row-major (K contiguous; e2m1 packs
@@ -101,14 +109,16 @@ typedef struct {
 typedef struct {
     int64_t num_tokens;          /* 0 <= T <= max_tokens; T = 0 writes no row of y                 */
     const void* x;               /* [T, H] e4m3 bytes, or bf16 for the BF16 recipe                  */
-    const uint8_t* x_sf;         /* [T, H/32] e8m0; NULL for BF16                                   */
+    const void* x_sf;            /* [T, H/32] e8m0 (FP8_BLOCK128: [T, H/128] fp32); NULL for BF16   */
     const int32_t* topk_idx;     /* [T, k] expert ids; -1 masks a slot                              */
     const float* topk_weights;   /* [T, k] combine weights                                          */
     const void* w1;              /* [E, 2I, H] (e2m1: [E, 2I, H/2] bytes); rows [0,I) gate, [I,2I) up; */
                                  /* in the problem's weight_layout                                   */
-    const uint8_t* w1_sf;        /* [E, 2I, H/32] e8m0 (or its TILED order); NULL for BF16           */
+    const void* w1_sf;           /* [E, 2I, H/32] e8m0 (or its TILED order; FP8_BLOCK128:            */
+                                 /* [E, 2I/128, H/128] fp32); NULL for BF16                          */
     const void* w2;              /* [E, H, I] (e2m1: [E, H, I/2] bytes), in the weight_layout       */
-    const uint8_t* w2_sf;        /* [E, H, I/32] e8m0 (or its TILED order); NULL for BF16           */
+    const void* w2_sf;           /* [E, H, I/32] e8m0 (or TILED; FP8_BLOCK128: [E, H/128, I/128]    */
+                                 /* fp32); NULL for BF16                                              */
     void* y;                     /* [T, H] of y_dtype; rows >= T untouched                          */
     int32_t y_dtype;             /* MOE_FFN_Y_*                                                      */
     float activation_clamp;      /* finite and > 0: clamp gate and up to [-c, c]; else no clamp      */

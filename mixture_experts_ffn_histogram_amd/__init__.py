@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_ffn.so")
 RECIPE_BF16 = 0
 RECIPE_FP8_FP8 = 1
 RECIPE_FP8_FP4 = 2
+RECIPE_FP8_BLOCK128 = 3
 WEIGHTS_ROW_MAJOR = 0
 WEIGHTS_TILED = 1
 Y_BF16 = 0

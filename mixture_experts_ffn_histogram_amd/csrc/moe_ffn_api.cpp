@@ -44,7 +44,7 @@ int check_problem(const moe_ffn_problem* p) {
   if (!p) return MOE_FFN_ERR_INVALID_ARG;
   if (p->max_tokens < 0 || p->hidden <= 0 || p->intermediate <= 0 || p->num_experts <= 0 || p->top_k <= 0)
     return MOE_FFN_ERR_INVALID_ARG;
-  if (p->recipe < MOE_FFN_RECIPE_BF16 || p->recipe > MOE_FFN_RECIPE_FP8_FP4) return MOE_FFN_ERR_INVALID_ARG;
+  if (p->recipe < MOE_FFN_RECIPE_BF16 || p->recipe > MOE_FFN_RECIPE_FP8_BLOCK128) return MOE_FFN_ERR_INVALID_ARG;
   if (p->weight_layout != MOE_FFN_WEIGHTS_ROW_MAJOR && p->weight_layout != MOE_FFN_WEIGHTS_TILED)
     return MOE_FFN_ERR_INVALID_ARG;
   if (p->weight_layout == MOE_FFN_WEIGHTS_TILED && p->recipe != MOE_FFN_RECIPE_FP8_FP4) return MOE_FFN_ERR_UNSUPPORTED;
@@ -60,8 +60,8 @@ int check_problem(const moe_ffn_problem* p) {
   // per-lane offsets): each of these byte ranges must stay below 2^31.
   const int64_t act = p->recipe == MOE_FFN_RECIPE_BF16 ? 2 : 1;  // bytes per x / h element
   const int64_t w1_bytes = p->recipe == MOE_FFN_RECIPE_BF16   ? 4 * p->intermediate * p->hidden
-                           : p->recipe == MOE_FFN_RECIPE_FP8_FP8 ? 2 * p->intermediate * p->hidden
-                                                                 : p->intermediate * p->hidden;
+                           : p->recipe == MOE_FFN_RECIPE_FP8_FP4 ? p->intermediate * p->hidden
+                                                                 : 2 * p->intermediate * p->hidden;
   if (p->max_tokens * p->hidden * act >= lim) return MOE_FFN_ERR_UNSUPPORTED;
   if ((p->max_tokens * p->top_k + moeffn::kMaxBM) * p->intermediate * act >= lim) return MOE_FFN_ERR_UNSUPPORTED;
   if (w1_bytes >= lim) return MOE_FFN_ERR_UNSUPPORTED;
@@ -74,8 +74,29 @@ int check_problem(const moe_ffn_problem* p) {
 int choose_block_m(int recipe, int64_t T, int64_t k, int64_t E) {
   const double avg = E > 0 ? double(T) * double(k) / double(E) : 0.0;
   int bm = avg <= 16.0 ? 16 : avg <= 40.0 ? 32 : avg <= 96.0 ? 64 : 128;
-  const int cap = moeffn::max_block_m(recipe);
-  return bm > cap ? cap : bm;
+  const int cap = moeffn::max_block_m(recipe), low = moeffn::min_block_m(recipe);
+  return bm > cap ? cap : bm < low ? low : bm;
+}
+
+// Workgroups a call can keep busy at most, from its sizes alone (the routing is
+// not known on the host): token blocks are at most S/bm + min(E, S) (every
+// expert with rows adds at most one partial block), each with I/32 (L1) and
+// H/64 (L2) wave tiles taken by 3 and 2 waves of a workgroup, or I/128 and
+// H/256 workgroup tiles; the combine has T * ceil(H/1024) units over 4 waves
+// per workgroup; large calls route with E columns.  A grid larger than this
+// only adds workgroups to every grid barrier (measured: ~0.24 us of barrier
+// time per workgroup on a 64-token call).
+int64_t useful_workgroups(int64_t T, int64_t H, int64_t I, int64_t E, int64_t k, int bm) {
+  const int64_t S = T * k;
+  const int64_t blocks = S / bm + (E < S ? E : S);
+  const bool wave = bm <= 32;
+  const int64_t l1 = wave ? (blocks * (I / 32) + 2) / 3 : blocks * ((I + 127) / 128);
+  const int64_t l2 = wave ? (blocks * (H / 64) + 1) / 2 : blocks * ((H + 255) / 256);
+  const int64_t comb = (T * ((H + 1023) / 1024) + 3) / 4;
+  int64_t n = l1 > l2 ? l1 : l2;
+  if (comb > n) n = comb;
+  if (S > moeffn::kLocalRouteSlots && E > n) n = E;
+  return n;
 }
 
 }  // namespace
@@ -101,7 +122,7 @@ int moe_ffn_get_workspace_size(const moe_ffn_problem* p, size_t* bytes) {
 }
 
 int moe_ffn_get_token_alignment(int32_t recipe, int64_t* alignment) {
-  if (!alignment || recipe < MOE_FFN_RECIPE_BF16 || recipe > MOE_FFN_RECIPE_FP8_FP4) return MOE_FFN_ERR_INVALID_ARG;
+  if (!alignment || recipe < MOE_FFN_RECIPE_BF16 || recipe > MOE_FFN_RECIPE_FP8_BLOCK128) return MOE_FFN_ERR_INVALID_ARG;
   *alignment = 1;
   return MOE_FFN_OK;
 }
@@ -225,7 +246,7 @@ int forward_enqueue(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   const int cus = physical_cus(dev);
   if (cus <= 0) return MOE_FFN_ERR_HIP;
   const int reserve = a->reserved_cus >= 0 ? a->reserved_cus : (int)env_long("MOE_FFN_RESERVED_CUS", 2);
-  const int grid = moe_ffn_launch_size(cus, reserve, a->max_cus);
+  int grid = moe_ffn_launch_size(cus, reserve, a->max_cus);
   const long timeout_ms = env_long("MOE_FFN_BARRIER_TIMEOUT_MS", 2000);
 
   uint8_t* ws = static_cast<uint8_t*>(workspace);
@@ -241,13 +262,13 @@ int forward_enqueue(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   k.timeout_ticks = (uint64_t)(timeout_ms > 0 ? timeout_ms : 1) * 100000ull;
   k.chunk_slots = L.chunk_slots;
   k.x = static_cast<const uint8_t*>(a->x);
-  k.x_sf = a->x_sf;
+  k.x_sf = static_cast<const uint8_t*>(a->x_sf);
   k.idx = a->topk_idx;
   k.tw = a->topk_weights;
   k.w1 = static_cast<const uint8_t*>(a->w1);
-  k.w1_sf = a->w1_sf;
+  k.w1_sf = static_cast<const uint8_t*>(a->w1_sf);
   k.w2 = static_cast<const uint8_t*>(a->w2);
-  k.w2_sf = a->w2_sf;
+  k.w2_sf = static_cast<const uint8_t*>(a->w2_sf);
   k.tiled = tiled ? 1 : 0;
   k.y = a->y;
   k.out_counts = a->expert_counts;
@@ -256,6 +277,7 @@ int forward_enqueue(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   k.out_s2r = a->slot_to_row;
   k.out_status = a->status;
   k.ctrl = reinterpret_cast<moeffn::Ctrl*>(ws + L.ctrl);
+  k.bars = reinterpret_cast<uint32_t*>(ws + L.bars);
   k.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   k.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   k.hist = reinterpret_cast<int32_t*>(ws + L.hist);
@@ -267,10 +289,14 @@ int forward_enqueue(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
 
   int bm = choose_block_m(recipe, T, p->top_k, p->num_experts);
   const long bm_env = env_long("MOE_FFN_BLOCK_M", 0);  // tuning override: 16, 32, 64 or 128
-  if ((bm_env == 16 || bm_env == 32 || bm_env == 64 || bm_env == 128) && bm_env <= moeffn::max_block_m(recipe))
+  if ((bm_env == 16 || bm_env == 32 || bm_env == 64 || bm_env == 128) && bm_env <= moeffn::max_block_m(recipe) &&
+      bm_env >= moeffn::min_block_m(recipe))
     bm = (int)bm_env;
   // the 128-row tiles read the TILED weight layout (and the stage-major scale copies of the workspace)
   if (bm == 128 && (!tiled || L.hsg == L.xsg)) bm = 64;
+  // a small call runs on fewer workgroups than the CU budget allows (never more)
+  const int64_t work = useful_workgroups(T, p->hidden, p->intermediate, p->num_experts, p->top_k, bm);
+  if (work < grid) grid = work < 2 ? 2 : (int)(work + (work & 1));
   if (env_long("MOE_FFN_LOG", 0) > 0)
     std::fprintf(stderr, "moe_ffn: T=%lld recipe=%d grid=%d (CUs %d, reserve %d, cap %d) block_m=%d\n",
                  (long long)T, recipe, grid, cus, reserve, a->max_cus, bm);

@@ -43,6 +43,7 @@ struct KParams {
   int32_t* out_status;
   // workspace views
   Ctrl* ctrl;
+  uint32_t* bars;          // barrier group counters (kBarGroups lines of kBarLineWords)
   int32_t* counts;
   int32_t* offsets;
   int32_t* hist;
@@ -72,8 +73,10 @@ hipError_t launch_transform_weights(const uint8_t* src, uint8_t* dst, int64_t E,
 hipError_t launch_transform_scales(const uint8_t* src, uint8_t* dst, int64_t E, int64_t rows, int64_t kb,
                                    hipStream_t stream);
 
-// Largest token block the recipe supports (register budget of the A ring).
+// Largest token block the recipe supports (register budget of the A ring), and the smallest (the
+// (1, 128, 128) recipe re-quantises whole 128-feature blocks, which only the 64-row tiles hold).
 int max_block_m(int recipe);
+int min_block_m(int recipe);
 
 // bf16 -> e4m3 + e8m0 per 1x32 block over n_elems elements (a multiple of 32).
 hipError_t launch_quantize_act(const uint16_t* x, uint8_t* q, uint8_t* sf, int64_t n_elems, hipStream_t stream);

@@ -56,6 +56,7 @@ template <int RECIPE, int BM>
 struct Cfg {
   static constexpr bool kBF16 = RECIPE == 0;
   static constexpr bool kW4 = RECIPE == 2;
+  static constexpr bool kB128 = RECIPE == 3;          // fp32 scales per 1x128 / 128x128 block
   static constexpr int KS = kBF16 ? 64 : 128;        // K elements per stage (128 bytes of a token row)
   static constexpr int ADW = kW4 ? 4 : 8;            // dwords of A per lane per 16-row block per stage
   static constexpr int NTB = BM / 16;                // 16-token blocks
@@ -111,17 +112,28 @@ __device__ __forceinline__ void raise_status(const KParams& p, int code, bool fa
   }
 }
 
-// Whole-grid barrier `id`: every workgroup arrives once per call.  The wait
-// is bounded: on timeout the call is aborted with ST_TIMEOUT.  Returns false
-// when the call is aborted.
-__device__ bool grid_barrier(const KParams& p, int id, Shared& sh) {
+// Whole-grid barrier `id`, the seq-th barrier of the call (from 0): every
+// workgroup arrives once per call, in two levels.  A workgroup counts itself
+// in its group's counter (group = blockIdx % 8, each counter on a 128-byte
+// line of its own, so the arrivals spread over 8 counters instead of queueing
+// G deep on one); the last workgroup of a group counts the group in the root
+// counter bar[id]; every workgroup waits until all groups are in.  A group
+// counter accumulates over the call's barriers: barrier seq is complete for a
+// group of n workgroups when it reaches (seq + 1) * n.  The wait is bounded:
+// on timeout the call is aborted with ST_TIMEOUT.  Returns false when the
+// call is aborted.
+__device__ bool grid_barrier(const KParams& p, int id, int seq, Shared& sh) {
   fence_release();
   __syncthreads();
   if (threadIdx.x == 0) {
     int ok = 1;
-    add_release(&p.ctrl->bar[id], 1u);
+    const uint32_t G = gridDim.x, grp = blockIdx.x % kBarGroups;
+    const uint32_t gsize = (G - grp + kBarGroups - 1) / kBarGroups;
+    const uint32_t groups = G < (uint32_t)kBarGroups ? G : (uint32_t)kBarGroups;
+    const uint32_t old = add_acq_rel(p.bars + grp * kBarLineWords, 1u);
+    if (old == (uint32_t)(seq + 1) * gsize - 1u) add_release(&p.ctrl->bar[id], 1u);
     const uint64_t t0 = now_ticks();
-    while (ld_relaxed(&p.ctrl->bar[id]) < gridDim.x) {
+    while (ld_relaxed(&p.ctrl->bar[id]) < groups) {
       if (ld_relaxed(&p.ctrl->abort)) { ok = 0; break; }
       if (now_ticks() - t0 > p.timeout_ticks) { raise_status(p, ST_TIMEOUT, true); ok = 0; break; }
       __builtin_amdgcn_s_sleep(1);
@@ -136,9 +148,9 @@ __device__ bool grid_barrier(const KParams& p, int id, Shared& sh) {
   return ok != 0;
 }
 
-// Entry check of the per-call state.  Every word of the control block must be
-// zero when a call starts (the workspace is zeroed once after allocation and
-// every call leaves it zeroed).  Workgroup 0 reads all of it before any
+// Entry check of the per-call state.  Every word of the control block and of
+// the barrier group counters must be zero when a call starts (the workspace
+// is zeroed once after allocation and every call leaves them zeroed).  Workgroup 0 reads all of it before any
 // workgroup of this call writes to it -- the others wait for its verdict --
 // so the check never sees this call's own counters.  A dirty block is
 // reported once (out_status = DIRTY_WORKSPACE), marked aborted so that no
@@ -152,7 +164,8 @@ __device__ uint32_t entry_verdict(const KParams& p, Shared& sh) {
   const int tid = threadIdx.x;
   uint32_t* words = reinterpret_cast<uint32_t*>(p.ctrl);
   if (blockIdx.x == 0) {
-    const uint32_t w = tid < kCtrlWords ? ld_relaxed(words + tid) : 0u;
+    uint32_t w = tid < kCtrlWords ? ld_relaxed(words + tid) : 0u;
+    for (int i = tid; i < kBarGroups * kBarLineWords; i += kThreads) w |= ld_relaxed(p.bars + i);
     const int nonzero = __syncthreads_or(w != 0u);
     if (tid == 0) {
       if (nonzero) {
@@ -428,19 +441,27 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
     active = i0 < I;
     arow[0] = i0; arow[1] = i0 + 16; arow[2] = I + i0; arow[3] = I + i0 + 16;
     W = p.w1 + (size_t)e * 2 * I * wrow_bytes;
-    Wsf = C::kBF16 ? nullptr : p.w1_sf + (size_t)e * 2 * I * wsf_row;
+    // (1, 128, 128): fp32 scales [E][2I/128][H/128]; else one e8m0 byte per row and 32-block
+    Wsf = C::kBF16 ? nullptr
+                   : p.w1_sf + (C::kB128 ? (size_t)e * (2 * I / 128) * (K / 128) * 4 : (size_t)e * 2 * I * wsf_row);
   } else {
     const int n0 = nb * 256 + wave * 64;
     active = n0 < H;
     arow[0] = n0; arow[1] = n0 + 16; arow[2] = n0 + 32; arow[3] = n0 + 48;
     W = p.w2 + (size_t)e * H * wrow_bytes;
-    Wsf = C::kBF16 ? nullptr : p.w2_sf + (size_t)e * H * wsf_row;
+    Wsf = C::kBF16 ? nullptr
+                   : p.w2_sf + (C::kB128 ? (size_t)e * (H / 128) * (K / 128) * 4 : (size_t)e * H * wsf_row);
   }
   const uint8_t* aptr[4];
   const uint8_t* sptr[4];
 #pragma unroll
   for (int j = 0; j < 4; j++) {
-    if constexpr (TILED) {
+    if constexpr (C::kB128) {
+      // e4m3 rows as for FP8 x FP8; the stage scales of the row's 128-row block: K/128 fp32 values
+      const size_t r = (size_t)(active ? arow[j] + r16 : r16);
+      aptr[j] = W + r * wrow_bytes + (size_t)g * 16;
+      sptr[j] = Wsf + (size_t)((active ? arow[j] : 0) / 128) * (size_t)(K / 128) * 4;
+    } else if constexpr (TILED) {
       // 16-row block of this row block (inactive waves stream block 0): weights at (blk * nk + s) KB,
       // scales of stage s at (blk * nk + 4 * (s / 4)) * 64 + r16 * 4 * n(s) + (s % 4) * 4
       const size_t blk = (size_t)(active ? arow[j] >> 4 : 0);
@@ -525,6 +546,21 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
           acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, ar[slot][j][1]),
                                                               __builtin_bit_cast(v8bf, b1), acc[j][t], 0, 0, 0);
         }
+      } else if constexpr (C::kB128) {
+        // unit block scales in the MFMA (byte 127 = 2^0); the stage's fp32 factors, weight block times
+        // token, are folded into the running sum with one FMA per element
+        const v8i bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        const float fb = __uint_as_float(sb.bsf[buf][t * 16 + r16]);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+          const v8i aa = {ar[slot][j][0][0], ar[slot][j][0][1], ar[slot][j][0][2], ar[slot][j][0][3],
+                          ar[slot][j][1][0], ar[slot][j][1][1], ar[slot][j][1][2], ar[slot][j][1][3]};
+          const v4f part = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
+                                                                            127, 0, 127);
+          const float f = __uint_as_float(sar[slot][j]) * fb;
+#pragma unroll
+          for (int c = 0; c < 4; c++) acc[j][t][c] = __builtin_fmaf(part[c], f, acc[j][t][c]);
+        }
       } else {
         const v8i bb = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
         const int sbv = (int)(sb.bsf[buf][t * 16 + r16] >> (8 * g));
@@ -579,6 +615,48 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
   }
   __syncthreads();  // every wave is done with the B stages before the next tile refills them
 
+  if constexpr (C::kB128) {
+    if (l1) {
+      // re-quantisation per 1x128 block of h: the tile's 128 features of a token are spread over the 4
+      // waves (32 each; every wave is active, I being a multiple of 128), so the block amax goes through
+      // LDS (the first B buffer, free now): s = max(fp32(amax / 448), smallest normal fp32), code = e4m3 of
+      // the IEEE fp32 quotient h / s
+      float* amx = reinterpret_cast<float*>(&sb.b[0][0]);
+#pragma unroll
+      for (int t = 0; t < C::NTB; t++) {
+        float a = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++)
+#pragma unroll
+          for (int j = 0; j < 4; j++)
+            a = __builtin_fmaxf(a, __builtin_fabsf(swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp)));
+        a = __builtin_fmaxf(a, __shfl_xor(a, 16, 64));
+        a = __builtin_fmaxf(a, __shfl_xor(a, 32, 64));
+        if (g == 0) amx[wave * 64 + t * 16 + r16] = a;
+      }
+      __syncthreads();
+      const int i0 = nb * 128 + wave * 32;
+#pragma unroll
+      for (int t = 0; t < C::NTB; t++) {
+        const int m = t * 16 + r16;
+        const float a = __builtin_fmaxf(__builtin_fmaxf(amx[m], amx[64 + m]), __builtin_fmaxf(amx[128 + m], amx[192 + m]));
+        const float sc = __builtin_fmaxf(a / 448.0f, 0x1p-126f);
+        if (m < nrows) {
+          const size_t row = (size_t)(row0 + m);
+#pragma unroll
+          for (int hh = 0; hh < 2; hh++) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+              word |= f32_to_e4m3(swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp) / sc) << (8 * j);
+            stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
+          }
+          if (wave == 0 && g == 0) stg4(p.h_sf + row * (size_t)(I / 32) + (size_t)nb * 4, __float_as_uint(sc));
+        }
+      }
+      return;
+    }
+  }
   if (!active) return;
   if (l1) {
     const int i0 = nb * 128 + wave * 32;
@@ -1600,20 +1678,20 @@ __device__ __forceinline__ void run_call(const KParams& p, Shared& sh, WaveCount
     } else {
       const int C = (S + (int)p.chunk_slots - 1) / (int)p.chunk_slots;
       phase_histogram(p, sh, S, C);
-      if (!grid_barrier(p, BAR_HIST, sh)) goto done;
+      if (!grid_barrier(p, BAR_HIST, 0, sh)) goto done;
       phase_column_scan(p, sh, C);
-      if (!grid_barrier(p, BAR_COLSCAN, sh)) goto done;
+      if (!grid_barrier(p, BAR_COLSCAN, 1, sh)) goto done;
       phase_scatter_global(p, sh, wcnt, S, C, BM);
-      if (!grid_barrier(p, BAR_SCATTER, sh)) goto done;
+      if (!grid_barrier(p, BAR_SCATTER, 2, sh)) goto done;
     }
     if constexpr (kBig) phase_big_tiles<RECIPE>(p, sh, *big, true);
     else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM, TILED>(p, sh, lr2s, local, true);
     else phase_wg_tiles<RECIPE, BM, TILED>(p, sh, *sb, lr2s, local, true);
-    if (!grid_barrier(p, BAR_L1, sh)) goto done;
+    if (!grid_barrier(p, BAR_L1, local ? 0 : 3, sh)) goto done;
     if constexpr (kBig) phase_big_tiles<RECIPE>(p, sh, *big, false);
     else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM, TILED>(p, sh, lr2s, local, false);
     else phase_wg_tiles<RECIPE, BM, TILED>(p, sh, *sb, lr2s, local, false);
-    if (!grid_barrier(p, BAR_L2, sh)) goto done;
+    if (!grid_barrier(p, BAR_L2, local ? 1 : 4, sh)) goto done;
     phase_combine(p);
   }
 done:
@@ -1629,6 +1707,7 @@ done:
       const int st = __hip_atomic_load(&p.ctrl->status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (p.out_status) *p.out_status = st;
       for (int i = 0; i < kNumBarriers; i++) st_relaxed(&p.ctrl->bar[i], 0u);
+      for (int g = 0; g < kBarGroups; g++) st_relaxed(p.bars + g * kBarLineWords, 0u);
       st_relaxed(&p.ctrl->tile_next, 0u);
       st_relaxed(&p.ctrl->tile_next2, 0u);
       for (int l = 0; l < 2; l++)
@@ -1662,6 +1741,7 @@ __global__ __launch_bounds__(kThreads, 2) void moe_ffn_kernel(KParams p) {
 }
 
 int max_block_m(int recipe) { return recipe == 2 ? 128 : 64; }
+int min_block_m(int recipe) { return recipe == 3 ? 64 : 16; }
 
 // ---------------------------------------------------------------------------
 // Weight-scale transform to the TILED layout: one thread per (expert, row,
@@ -1723,14 +1803,18 @@ static hipError_t launch_one(int grid, const KParams& p, hipStream_t stream) {
 
 template <int RECIPE, bool TILED>
 static hipError_t launch_recipe(int bm, int grid, const KParams& p, hipStream_t stream) {
-  switch (bm) {
-    case 16: return launch_one<RECIPE, 16, TILED>(grid, p, stream);
-    case 32: return launch_one<RECIPE, 32, TILED>(grid, p, stream);
-    case 64: return launch_one<RECIPE, 64, TILED>(grid, p, stream);
-    case 128:
-      if constexpr (RECIPE == 2 && TILED) return launch_one<RECIPE, 128, TILED>(grid, p, stream);
-      return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
+  if constexpr (RECIPE == 3) {   // the (1, 128, 128) recipe runs on the 64-row workgroup tiles only
+    return bm == 64 ? launch_one<RECIPE, 64, TILED>(grid, p, stream) : hipErrorInvalidValue;
+  } else {
+    switch (bm) {
+      case 16: return launch_one<RECIPE, 16, TILED>(grid, p, stream);
+      case 32: return launch_one<RECIPE, 32, TILED>(grid, p, stream);
+      case 64: return launch_one<RECIPE, 64, TILED>(grid, p, stream);
+      case 128:
+        if constexpr (RECIPE == 2 && TILED) return launch_one<RECIPE, 128, TILED>(grid, p, stream);
+        return hipErrorInvalidValue;
+      default: return hipErrorInvalidValue;
+    }
   }
 }
 
@@ -1739,6 +1823,7 @@ hipError_t launch_forward(int recipe, int bm, bool tiled, int grid, const KParam
     case 0: return tiled ? hipErrorInvalidValue : launch_recipe<0, false>(bm, grid, p, stream);
     case 1: return tiled ? hipErrorInvalidValue : launch_recipe<1, false>(bm, grid, p, stream);
     case 2: return tiled ? launch_recipe<2, true>(bm, grid, p, stream) : launch_recipe<2, false>(bm, grid, p, stream);
+    case 3: return tiled ? hipErrorInvalidValue : launch_recipe<3, false>(bm, grid, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -40,10 +40,19 @@ static_assert(offsetof(Ctrl, xq) == 44, "layout change must be deliberate");
 static_assert(offsetof(Ctrl, verdict) == 108, "layout change must be deliberate");
 constexpr int kCtrlWords = (int)(sizeof(Ctrl) / 4);
 
+// Grid-barrier group counters, right after the control block: 8 groups of
+// workgroups (blockIdx % 8), one 128-byte line each, counting the arrivals of
+// the group's workgroups over all barriers of a call.  Zero between calls.
+constexpr int kBarGroups = 8;
+constexpr int kBarLineWords = 32;
+constexpr int kBarRegionBytes = kBarGroups * kBarLineWords * 4;
+// Bytes at the start of the workspace that must be zero when a call starts.
+constexpr int kCtrlRegionBytes = (int)sizeof(Ctrl) + kBarRegionBytes;
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-  size_t ctrl, counts, offsets, hist, r2s, s2r, h, h_sf, o, xsg, hsg, total;
+  size_t ctrl, bars, counts, offsets, hist, r2s, s2r, h, h_sf, o, xsg, hsg, total;
   int64_t chunk_slots;   // slots per routing chunk
   int64_t max_slots;     // max_tokens * k
   int64_t h_rows;        // rows of h (max_slots + kMaxBM padding)
@@ -64,6 +73,7 @@ inline Layout make_layout(int64_t max_tokens, int64_t H, int64_t I, int64_t E, i
   L.o_row_bytes = H * 4;
   size_t off = 0;
   L.ctrl = off;    off = align_up(off + sizeof(Ctrl), A);
+  L.bars = off;    off = align_up(off + kBarRegionBytes, A);
   L.counts = off;  off = align_up(off + sizeof(int32_t) * (size_t)E, A);
   L.offsets = off; off = align_up(off + sizeof(int32_t) * (size_t)(E + 1), A);
   L.hist = off;    off = align_up(off + sizeof(int32_t) * (size_t)kMaxChunks * (size_t)E, A);

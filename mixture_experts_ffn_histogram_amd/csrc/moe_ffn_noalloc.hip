@@ -7,8 +7,9 @@
 // the first call on a device (with that device current) asks the runtime for
 // the array's address on that device and keeps it; every launch, copy and
 // clear uses that address.  Each call first clears the control block (the
-// only part of the workspace that must be zero when a call starts) with a
-// small kernel on the call's stream, then runs the ordinary forward.  All calls
+// part of the workspace that must be zero when a call starts) with a
+// small kernel on the call's stream (with the barrier counters behind it), then
+// runs the ordinary forward.  All calls
 // on one GPU share the array, so calls that overlap on one GPU race.
 #include <hip/hip_runtime.h>
 
@@ -27,11 +28,14 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<void*> g_scratch[kMaxDevices];
 
-__global__ void clear_ctrl_kernel(uint32_t* words) { words[threadIdx.x] = 0u; }
+__global__ void clear_ctrl_kernel(uint32_t* words) {
+  for (int i = threadIdx.x; i < moeffn::kCtrlRegionBytes / 4; i += blockDim.x) words[i] = 0u;
+}
 
+// Clears the control block and the barrier counters behind it (the part of
+// the workspace that must be zero when a call starts).
 hipError_t clear_ctrl(void* workspace, hipStream_t stream) {
-  hipLaunchKernelGGL(clear_ctrl_kernel, dim3(1), dim3(moeffn::kCtrlWords), 0, stream,
-                     static_cast<uint32_t*>(workspace));
+  hipLaunchKernelGGL(clear_ctrl_kernel, dim3(1), dim3(256), 0, stream, static_cast<uint32_t*>(workspace));
   return hipGetLastError();
 }
 

@@ -72,7 +72,7 @@ class Config:
         return replace(self, **kw)
 
 
-# The five workloads.  Names state what they are.
+# The five workloads, and one of the (1, 128, 128) recipe.  Names state what they are.
 CONFIGS = {
     "bf16_T64_H256_I128_E8_k2": Config("bf16_T64_H256_I128_E8_k2", RECIPE_BF16, 64, 256, 128, 8, 2,
                                        "softmax", 101, y_fp32=True),
@@ -84,6 +84,9 @@ CONFIGS = {
                                           "zipf", 404),
     "deepseek_fp8xfp4_T32768_zipf": Config("deepseek_fp8xfp4_T32768_zipf", RECIPE_FP8_FP4, 32768, 7168, 2048, 256,
                                            8, "zipf", 505),
+    # the (1, 128, 128) fp32-scale recipe at the FP8 x FP8 workload's shape
+    "fp8block128_T512_H2048_I768_E64_k6": Config("fp8block128_T512_H2048_I768_E64_k6", RECIPE_FP8_B128, 512, 2048,
+                                                 768, 64, 6, "uniform", 606),
 }
 
 # tensor ids for seed derivation

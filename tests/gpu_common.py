@@ -179,6 +179,9 @@ def w2_abs_cols(p: dict, e: int, cols: np.ndarray) -> np.ndarray:
     """|W2(e, n, i)| for all n < H and i in cols, dequantised: [H, len(cols)] float64."""
     e4, e2 = _codec_tables()
     cols = np.asarray(cols, np.int64)
+    if p["recipe"] == synth.RECIPE_FP8_B128:   # fp32 factor per 128 x 128 block
+        scale = np.repeat(p["w2_sf"][e][:, cols // 128].astype(np.float64), 128, axis=0)
+        return np.abs(e4[p["w2"][e][:, cols]] * scale)
     scale = np.ldexp(1.0, p["w2_sf"][e][:, cols // 32].astype(np.int32) - 127)
     if p["recipe"] == synth.RECIPE_FP8_FP4:
         b = p["w2"][e][:, cols // 2]
@@ -201,6 +204,15 @@ def workspace_h_rows(run: "Runner", rows) -> tuple[np.ndarray, np.ndarray]:
     return ws[ci].cpu().numpy(), ws[si].cpu().numpy()
 
 
+def h_values(p: dict, codes: np.ndarray, sfs: np.ndarray) -> np.ndarray:
+    """Values of one re-quantised row from its e4m3 codes and its scales (e8m0 per 1x32, or one fp32
+    factor per 1x128 for the (1, 128, 128) recipe)."""
+    e4, _ = _codec_tables()
+    if p["recipe"] == synth.RECIPE_FP8_B128:
+        return e4[codes] * np.repeat(np.ascontiguousarray(sfs).view(np.float32).astype(np.float64), 128)
+    return e4[codes] * np.repeat(np.ldexp(1.0, sfs.astype(np.int32) - 127), 32)
+
+
 def scan_flips(p: dict, toks, s2r: np.ndarray, codes: np.ndarray, sfs: np.ndarray, hq: np.ndarray,
                delta: np.ndarray) -> tuple[np.ndarray, dict]:
     """Compare the GPU's re-quantised rows with the oracle's, for every valid
@@ -208,12 +220,16 @@ def scan_flips(p: dict, toks, s2r: np.ndarray, codes: np.ndarray, sfs: np.ndarra
     in (token, slot) order).  Every value that differs must lie inside the
     oracle's band (|h_gpu - h_ref| <= delta), else the test fails.  Returns the
     allowance on y that the differing values can cause,
-        allow[q, n] = sum_j |w[t, j]| * sum_i |h_gpu - h_ref|_i * |W2(e_j, n, i)|,
-    and counts (differing elements, 32-blocks holding one)."""
-    e4, _ = _codec_tables()
+        allow[q, n] = sum_j |w[t, j]| * sum_i |h_gpu - h_ref|_i * |W2(e_j, n, i)|
+    (summed per expert as one product of |W2(e)| with the rows' differences),
+    and counts: rows, re-quantisation flips (a code that changed: more than
+    2^-16 of the value apart, finer than any e4m3 step; the fp32-scale recipe
+    also moves every value of a block by its scale's last bits) and the
+    32-element blocks holding one."""
     k, H, E = p["k"], p["H"], p["E"]
     idx, w = p["topk_idx"], p["topk_weights"]
     allow = np.zeros((len(toks), H), np.float64)
+    per_expert = {}
     flips = blocks = nrows = 0
     n = 0
     for q, t in enumerate(toks):
@@ -222,18 +238,24 @@ def scan_flips(p: dict, toks, s2r: np.ndarray, codes: np.ndarray, sfs: np.ndarra
             if not (0 <= e < E):
                 continue
             assert s2r[t * k + j] >= 0
-            g = e4[codes[n]] * np.repeat(np.ldexp(1.0, sfs[n].astype(np.int32) - 127), 32)
+            g = h_values(p, codes[n], sfs[n])
             d = g - hq[q, j]
             bad = np.abs(d) > delta[q, j]
             assert not bad.any(), (f"token {t} slot {j} (expert {e}): {int(bad.sum())} re-quantised values outside "
                                    f"the rounding-decision band, first at i={np.where(bad)[0][:5]}")
-            nz = np.nonzero(d)[0]
-            if nz.size:
-                allow[q] += abs(float(w[t, j])) * (w2_abs_cols(p, e, nz) @ np.abs(d[nz]))
-                flips += int(nz.size)
-                blocks += int(np.unique(nz // 32).size)
+            if np.any(d):
+                per_expert.setdefault(e, []).append((q, abs(float(w[t, j])), np.abs(d)))
+            flip = np.abs(d) > np.abs(hq[q, j]) * 2.0 ** -16
+            flips += int(flip.sum())
+            blocks += int(np.unique(np.nonzero(flip)[0] // 32).size)
             nrows += 1
             n += 1
+    for e, items in per_expert.items():
+        D = np.stack([a for _, _, a in items], axis=1)                # [I, rows]
+        cols = np.nonzero(D.any(axis=1))[0]
+        contrib = w2_abs_cols(p, e, cols) @ D[cols]                    # [H, rows]
+        for c, (q, wt, _) in enumerate(items):
+            allow[q] += wt * contrib[:, c]
     return allow, {"rows": nrows, "flips": flips, "flip_blocks": blocks}
 
 
@@ -277,6 +299,7 @@ def check_collected(p: dict, toks, col: dict, what: str, clamp: float | None = N
     """The oracle side of fp8_parity, on what collect_gpu brought back."""
     clamp = p["clamp"] if clamp is None else clamp
     assert col["status32"] == status, f"{what}: device status {col['status32']}"
+    log(f"  {what}: oracle on {len(toks)} tokens")
     ref32, hq, delta, _ = oracle.forward_tokens_rows(p, toks, True, clamp, RHO)
     ref32 = ref32.astype(np.float64)
     allow, fl = scan_flips(p, toks, col["s2r"], col["codes"], col["sfs"], hq, delta)
@@ -357,7 +380,7 @@ def check_tile_rows(run: "Runner", p: dict, rows, what: str, clamp: float | None
     flips = 0
     worst = 0.0
     for i, ref in enumerate(refs):
-        g = e4[codes[i]] * np.repeat(np.ldexp(1.0, sfs[i].astype(np.int32) - 127), 32)
+        g = h_values(p, codes[i], sfs[i])
         d = g - ref["hq"]
         bad = np.abs(d) > ref["delta"]
         assert not bad.any(), f"{what}: row {rows[i]}: {int(bad.sum())} codes outside the band"

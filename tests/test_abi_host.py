@@ -61,7 +61,7 @@ def test_workspace_size_depends_on_problem_only_and_grows_with_tokens():
 
 
 def test_token_alignment_and_strerror():
-    for r in (mf.RECIPE_BF16, mf.RECIPE_FP8_FP8, mf.RECIPE_FP8_FP4):
+    for r in (mf.RECIPE_BF16, mf.RECIPE_FP8_FP8, mf.RECIPE_FP8_FP4, mf.RECIPE_FP8_BLOCK128):
         assert mf.get_token_alignment(r) == 1
     with pytest.raises(mf.MoeFFNError):
         mf.get_token_alignment(7)
@@ -77,7 +77,9 @@ def test_token_alignment_and_strerror():
     ((16, 256, 128, 8, 65, mf.RECIPE_FP8_FP4), mf.ERR_UNSUPPORTED),   # top-k too large
     ((-1, 256, 128, 8, 2, mf.RECIPE_FP8_FP4), mf.ERR_INVALID_ARG),
     ((16, 256, 128, 0, 2, mf.RECIPE_FP8_FP4), mf.ERR_INVALID_ARG),
-    ((16, 256, 128, 8, 2, 3), mf.ERR_INVALID_ARG),
+    ((16, 256, 128, 8, 2, 4), mf.ERR_INVALID_ARG),                                    # no such recipe
+    ((16, 192, 128, 8, 2, mf.RECIPE_FP8_BLOCK128), mf.ERR_UNSUPPORTED),               # H not a multiple of 128
+    ((16, 256, 128, 8, 2, mf.RECIPE_FP8_BLOCK128, mf.WEIGHTS_TILED), mf.ERR_UNSUPPORTED),
     ((16, 256, 128, 8, 2, mf.RECIPE_FP8_FP4, 2), mf.ERR_INVALID_ARG),               # no such weight layout
     ((16, 256, 128, 8, 2, mf.RECIPE_BF16, mf.WEIGHTS_TILED), mf.ERR_UNSUPPORTED),   # TILED holds e2m1 only
     ((16, 256, 128, 8, 2, mf.RECIPE_FP8_FP8, mf.WEIGHTS_TILED), mf.ERR_UNSUPPORTED),

@@ -285,8 +285,10 @@ def test_large_call_row_major_uses_64_row_tiles(monkeypatch):
 
 
 # Control-block words (32-bit) of the workspace: bar[0..5], exit_count 6,
-# tile_next 7, tile_next2 8, abort 9, status 10, xq 11..26, verdict 27, pad 28..63.
-@pytest.mark.parametrize("word,value", [(6, 5), (6, 1 << 30), (2, 1), (9, 1), (27, 1), (50, 7)])
+# tile_next 7, tile_next2 8, abort 9, status 10, xq 11..26, verdict 27, pad 28..63;
+# then the barrier group counters, one 128-byte line per group (words 64, 96, ..., 288).
+@pytest.mark.parametrize("word,value", [(6, 5), (6, 1 << 30), (2, 1), (9, 1), (27, 1), (50, 7), (64, 3), (96, 1),
+                                        (300, 2)])
 def test_dirty_workspace_reported_without_waiting(word, value):
     import time
     cfg = _small_cfg(synth.RECIPE_FP8_FP4, 64, 256, 128, 8, 2, "softmax", seed=17)
@@ -296,7 +298,7 @@ def test_dirty_workspace_reported_without_waiting(word, value):
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     y_ref = run.y.clone()
-    ctrl = run.m.workspace[:256].view(torch.int32)
+    ctrl = run.m.workspace[:1280].view(torch.int32)
     ctrl[word] = value
     torch.cuda.synchronize()
     log(f"dirty control word {word} = {value}")
@@ -312,4 +314,4 @@ def test_dirty_workspace_reported_without_waiting(word, value):
     torch.cuda.synchronize()
     assert int(run.status.item()) == 0
     assert torch.equal(run.y, y_ref)
-    assert not bool(run.m.workspace[:256].any()), "a clean call must leave the control block zeroed"
+    assert not bool(run.m.workspace[:1280].any()), "a clean call must leave the control block zeroed"
