@@ -1042,8 +1042,10 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
     }
   };
 
-  // Earlier stores and loads of this wave must not be counted as ring fills.
-  MOEFFN_WAIT_VMCNT(0);
+  // No drain here: vector-memory operations issued before the ring (the
+  // previous tile's stores, the tile claim in flight) only make the count
+  // waits below stricter, since the ring's own operations complete in issue
+  // order, and they can complete under the prologue's loads.
   // Prologue, in the steady issue order: virtual iterations -P..-1 each issue
   // the fill of stage it + D, then the weight loads of stage it + P.
   load_a(0, 0);
@@ -1551,18 +1553,30 @@ __device__ __forceinline__ void decode_big_tile(const Shared& sh, int E, int NB,
   mb = c * kBigGM + (j - nb * gm);
 }
 
-// Claim the next tile (thread 0): own XCD's range first, then the others.
-// Returns n when every range is exhausted (or the queue is closed).
-__device__ __forceinline__ uint32_t claim_big_tile(uint32_t* ctr, uint32_t n, int home) {
-  for (int q = 0; q < 8; q++) {
-    const int r = (home + q) & 7;
-    const uint32_t beg = (uint32_t)(((uint64_t)n * (uint32_t)r) >> 3);
-    const uint32_t end = (uint32_t)(((uint64_t)n * (uint32_t)(r + 1)) >> 3);
-    if (end == beg) continue;
-    if (ld_relaxed(&ctr[r]) >= end - beg) continue;  // already drained: skip the atomic
-    const uint32_t c = __hip_atomic_fetch_add(&ctr[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (c < end - beg) return beg + c;
+__device__ __forceinline__ uint32_t big_range_begin(uint32_t n, int r) {
+  return (uint32_t)(((uint64_t)n * (uint32_t)r) >> 3);
+}
+
+// Turn a claim into a tile (thread 0).  `c` is the value a fetch-and-add on
+// range `cur`'s counter returned; once that range is drained the other ranges
+// are tried in turn, synchronously (only at the end of a phase), and `cur`
+// moves to the range that yields a tile.  Returns n when every range is
+// exhausted.
+__device__ __forceinline__ uint32_t resolve_big_claim(uint32_t* ctr, uint32_t n, int& cur, uint32_t c) {
+  const uint32_t beg = big_range_begin(n, cur), end = big_range_begin(n, cur + 1);
+  if (c < end - beg) return beg + c;
+  for (int q = 1; q < 8; q++) {
+    const int r = (cur + q) & 7;
+    const uint32_t b = big_range_begin(n, r), e = big_range_begin(n, r + 1);
+    if (e == b) continue;
+    if (ld_relaxed(&ctr[r]) >= e - b) continue;  // already drained: skip the atomic
+    const uint32_t v = __hip_atomic_fetch_add(&ctr[r], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (v < e - b) {
+      cur = r;
+      return b + v;
+    }
   }
+  cur = (cur + 7) & 7;  // every range is drained; later claims resolve to n as well
   return n;
 }
 
@@ -1573,16 +1587,20 @@ __device__ __forceinline__ void phase_big_tiles(const KParams& p, Shared& sh, co
   const int NB = l1 ? p.I / 128 : (p.H + 255) / 256;
   const uint32_t n = (uint32_t)(sh.mbo[E] * NB);
   uint32_t* ctr = p.ctrl->xq[l1 ? 0 : 1];
-  const int home = xcc_id();
-  uint32_t next = 0;
-  if (tid == 0) next = claim_big_tile(ctr, n, home);
+  // Thread 0 keeps one claim in flight while a tile runs: a fetch-and-add on
+  // the counter of range `cur` (first the XCD's own), issued before the tile
+  // and resolved after it, so its round trip to the memory-side atomics
+  // overlaps the tile instead of standing between two tiles.
+  int cur = xcc_id();
+  uint32_t pend = 0;
+  if (tid == 0) pend = __hip_atomic_fetch_add(&ctr[cur], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   for (;;) {
-    if (tid == 0) sh.tile = next;
+    if (tid == 0) sh.tile = resolve_big_claim(ctr, n, cur, pend);
     __syncthreads();
     const uint32_t t = __builtin_amdgcn_readfirstlane(sh.tile);
     __syncthreads();
     if (t >= n) break;
-    if (tid == 0) next = claim_big_tile(ctr, n, home);
+    if (tid == 0) pend = __hip_atomic_fetch_add(&ctr[cur], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int e, mb, nb;
     decode_big_tile(sh, E, NB, (int)t, e, mb, nb);
     e = __builtin_amdgcn_readfirstlane(e);
