@@ -260,7 +260,6 @@ int forward_enqueue(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   k.clamp_on = std::isfinite(a->activation_clamp) && a->activation_clamp > 0.0f;
   k.clamp = k.clamp_on ? a->activation_clamp : 0.0f;
   k.timeout_ticks = (uint64_t)(timeout_ms > 0 ? timeout_ms : 1) * 100000ull;
-  k.chunk_slots = L.chunk_slots;
   k.x = static_cast<const uint8_t*>(a->x);
   k.x_sf = static_cast<const uint8_t*>(a->x_sf);
   k.idx = a->topk_idx;

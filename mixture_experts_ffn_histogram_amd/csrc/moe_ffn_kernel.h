@@ -24,7 +24,6 @@ struct KParams {
   float clamp;
   int32_t tiled;           // weights (and their scales) in the TILED layout (e2m1 recipe)
   uint64_t timeout_ticks;  // bound on every wait, in 100 MHz realtime ticks
-  int64_t chunk_slots;     // routing chunk size
   // inputs
   const uint8_t* x;
   const uint8_t* x_sf;

@@ -4,13 +4,15 @@
 // Routing, small calls (T*k <= kLocalRouteSlots): every workgroup builds the
 // routing tables of the whole call in its own LDS (histogram, prefix sums,
 // stable ranks); workgroup 0 publishes them.  Large calls:
-//   R1  per-chunk expert histogram of topk_idx              -- grid barrier 0
-//   R2  per-expert column scan over the chunks -> counts    -- grid barrier 1
-//   R3  prefix sums in LDS (every workgroup); stable scatter -- grid barrier 2
+//   R1  per-chunk expert histogram of topk_idx (one chunk per workgroup at
+//       most)                                                -- grid barrier 0
+//   R2  every workgroup reads the whole per-chunk histogram: expert totals,
+//       prefix sums in LDS, the first row of each expert in its own chunk;
+//       stable scatter of its chunk                          -- grid barrier 1
 // Then, for every call:
 //   L1  tile queue of L1 tiles: gathered x rows x W1 on scaled MFMA, fused
-//       SwiGLU + clamp + 1x32 e8m0 re-quantisation -> h      -- grid barrier 3
-//   L2  tile queue of L2 tiles: h x W2 -> fp32 o per routed row -- grid barrier 4
+//       SwiGLU + clamp + 1x32 e8m0 re-quantisation -> h      -- grid barrier 2
+//   L2  tile queue of L2 tiles: h x W2 -> fp32 o per routed row -- grid barrier 3
 //   C   combine: y[t] = sum over valid slots j (ascending) of w[t,j] o[row]
 //   X   the last workgroup out re-zeroes the control block.
 // The stages follow the method of the MegaMoE pages: dispatch (expert count,
@@ -50,7 +52,7 @@ namespace moeffn {
 
 enum { ST_OK = 0, ST_BAD_EXPERT_INDEX = 1, ST_TIMEOUT = 2, ST_DIRTY = 3 };
 constexpr uint32_t kQueueClosed = 0x80000000u;
-enum { BAR_HIST = 0, BAR_COLSCAN = 1, BAR_SCATTER = 2, BAR_L1 = 3, BAR_L2 = 4 };
+enum { BAR_HIST = 0, BAR_SCATTER = 1, BAR_L1 = 2, BAR_L2 = 3 };
 
 template <int RECIPE, int BM>
 struct Cfg {
@@ -72,6 +74,7 @@ struct Shared {
   int off[kMaxExperts + 1];     // expert row offsets
   int mbo[kMaxExperts + 1];     // expert token-block offsets
   int cnt[kMaxExperts];         // expert counts / histogram scratch
+  int pfx[kMaxExperts];         // rows of each expert in the routing chunks before this workgroup's
   int scan[4];
   int flag;
   uint32_t tile;
@@ -199,15 +202,15 @@ __device__ uint32_t entry_verdict(const KParams& p, Shared& sh) {
 // ---------------------------------------------------------------------------
 // Routing
 // ---------------------------------------------------------------------------
-// R1 (large calls): per-chunk histograms.
-__device__ void phase_histogram(const KParams& p, Shared& sh, int S, int C) {
+// R1 (large calls): per-chunk histograms, chunk c = slots [c * cs, (c + 1) * cs).
+__device__ void phase_histogram(const KParams& p, Shared& sh, int S, int C, int cs) {
   const int tid = threadIdx.x;
   int bad = 0;
   for (int c = blockIdx.x; c < C; c += gridDim.x) {
     for (int e = tid; e < p.E; e += kThreads) sh.cnt[e] = 0;
     __syncthreads();
-    const int beg = c * (int)p.chunk_slots;
-    const int end = min(S, beg + (int)p.chunk_slots);
+    const int beg = c * cs;
+    const int end = min(S, beg + cs);
     for (int s = beg + tid; s < end; s += kThreads) {
       const int e = p.idx[s];
       if ((unsigned)e < (unsigned)p.E) atomicAdd(&sh.cnt[e], 1);
@@ -218,18 +221,6 @@ __device__ void phase_histogram(const KParams& p, Shared& sh, int S, int C) {
     __syncthreads();
   }
   if (bad) raise_status(p, ST_BAD_EXPERT_INDEX, false);
-}
-
-// R2 (large calls): column scan over chunks for each expert.
-__device__ void phase_column_scan(const KParams& p, Shared& sh, int C) {
-  const int tid = threadIdx.x;
-  for (int e = blockIdx.x; e < p.E; e += gridDim.x) {
-    const int v = tid < C ? p.hist[(size_t)tid * p.E + e] : 0;
-    int total;
-    const int pre = block_excl_scan(v, sh.scan, &total);
-    if (tid < C) p.hist[(size_t)tid * p.E + e] = pre;
-    if (tid == 0) p.counts[e] = total;
-  }
 }
 
 // Exclusive scan of src[0..E) into dst[0..E], dst[E] = total (E <= 512).
@@ -329,8 +320,18 @@ __device__ void scatter_range(const KParams& p, Shared& sh, WaveCounters& wcnt, 
         p.r2s[row] = s;
         p.s2r[s] = row;
         if (p.xsg) {  // the token's activation scales, one dword per K stage, to the row's column
+          // (8 loads issued before their 8 stores: the two buffers may alias as far as the
+          // compiler knows, so a load after a store would wait for the store's round trip)
           const uint32_t* src = reinterpret_cast<const uint32_t*>(p.x_sf) + (size_t)(s / p.k) * (size_t)(p.H >> 7);
-          for (int st = 0; st < (p.H >> 7); st++) p.xsg[(size_t)st * p.sg_rows + row] = src[st];
+          const int nst = p.H >> 7;
+          for (int st0 = 0; st0 < nst; st0 += 8) {
+            uint32_t v[8];
+#pragma unroll
+            for (int j = 0; j < 8; j++) v[j] = st0 + j < nst ? src[st0 + j] : 0u;
+#pragma unroll
+            for (int j = 0; j < 8; j++)
+              if (st0 + j < nst) p.xsg[(size_t)(st0 + j) * p.sg_rows + row] = v[j];
+          }
         }
         if (p.out_r2s) p.out_r2s[row] = s;
         if (p.out_s2r) p.out_s2r[s] = row;
@@ -362,17 +363,38 @@ __device__ void phase_route_local(const KParams& p, Shared& sh, WaveCounters& wc
   scatter_range(p, sh, wcnt, 0, S, nullptr, lr2s, blockIdx.x == 0);
 }
 
-// Large call, R3: tables from the column scan, then the chunk scatter.
-__device__ void phase_scatter_global(const KParams& p, Shared& sh, WaveCounters& wcnt, int S, int C, int bm) {
+// Large call, R2: every workgroup reads the whole per-chunk histogram (C <= 256
+// rows of E counts, coalesced across the threads, eight rows in flight): the
+// expert totals give the tables, the counts of the chunks before its own the
+// first row of each expert inside its chunk (C <= gridDim.x: one chunk per
+// workgroup at most); then the stable scatter of its chunk.
+__device__ void phase_scatter_global(const KParams& p, Shared& sh, WaveCounters& wcnt, int S, int C, int cs, int bm) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < p.E; e += kThreads) sh.cnt[e] = p.counts[e];
+  const int own = blockIdx.x;
+  for (int e = tid; e < p.E; e += kThreads) {
+    int total = 0, before = 0, c = 0;
+    for (; c + 8 <= C; c += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) v[j] = p.hist[(size_t)(c + j) * p.E + e];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        total += v[j];
+        before += c + j < own ? v[j] : 0;
+      }
+    }
+    for (; c < C; c++) {
+      const int v = p.hist[(size_t)c * p.E + e];
+      total += v;
+      before += c < own ? v : 0;
+    }
+    sh.cnt[e] = total;
+    sh.pfx[e] = before;
+  }
   __syncthreads();
   build_tables(p, sh, wcnt, bm);
   if (blockIdx.x == 0) publish_tables(p, sh);
-  for (int c = blockIdx.x; c < C; c += gridDim.x) {
-    const int beg = c * (int)p.chunk_slots;
-    scatter_range(p, sh, wcnt, beg, min(S, beg + (int)p.chunk_slots), p.hist + (size_t)c * p.E, nullptr, true);
-  }
+  if (own < C) scatter_range(p, sh, wcnt, own * cs, min(S, (own + 1) * cs), sh.pfx, nullptr, true);
 }
 
 // ---------------------------------------------------------------------------
@@ -1694,22 +1716,23 @@ __device__ __forceinline__ void run_call(const KParams& p, Shared& sh, WaveCount
     if (local) {
       phase_route_local(p, sh, wcnt, lr2s, S, BM);
     } else {
-      const int C = (S + (int)p.chunk_slots - 1) / (int)p.chunk_slots;
-      phase_histogram(p, sh, S, C);
+      // chunks of a multiple of 64 slots, at most one per workgroup and kMaxChunks in all
+      const int cmax = min((int)gridDim.x, kMaxChunks);
+      const int cs = max(64, ((S + cmax - 1) / cmax + 63) / 64 * 64);
+      const int C = (S + cs - 1) / cs;
+      phase_histogram(p, sh, S, C, cs);
       if (!grid_barrier(p, BAR_HIST, 0, sh)) goto done;
-      phase_column_scan(p, sh, C);
-      if (!grid_barrier(p, BAR_COLSCAN, 1, sh)) goto done;
-      phase_scatter_global(p, sh, wcnt, S, C, BM);
-      if (!grid_barrier(p, BAR_SCATTER, 2, sh)) goto done;
+      phase_scatter_global(p, sh, wcnt, S, C, cs, BM);
+      if (!grid_barrier(p, BAR_SCATTER, 1, sh)) goto done;
     }
     if constexpr (kBig) phase_big_tiles<RECIPE>(p, sh, *big, true);
     else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM, TILED>(p, sh, lr2s, local, true);
     else phase_wg_tiles<RECIPE, BM, TILED>(p, sh, *sb, lr2s, local, true);
-    if (!grid_barrier(p, BAR_L1, local ? 0 : 3, sh)) goto done;
+    if (!grid_barrier(p, BAR_L1, local ? 0 : 2, sh)) goto done;
     if constexpr (kBig) phase_big_tiles<RECIPE>(p, sh, *big, false);
     else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM, TILED>(p, sh, lr2s, local, false);
     else phase_wg_tiles<RECIPE, BM, TILED>(p, sh, *sb, lr2s, local, false);
-    if (!grid_barrier(p, BAR_L2, local ? 1 : 4, sh)) goto done;
+    if (!grid_barrier(p, BAR_L2, local ? 1 : 3, sh)) goto done;
     phase_combine(p);
   }
 done:

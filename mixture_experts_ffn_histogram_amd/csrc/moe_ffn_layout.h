@@ -13,8 +13,7 @@ namespace moeffn {
 constexpr int kThreads = 256;          // one workgroup = 4 waves of 64
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 64;
-constexpr int kMaxChunks = 256;        // routing chunks (one per thread in the column scan)
-constexpr int kMinChunkSlots = 1024;   // routing chunk granularity
+constexpr int kMaxChunks = 256;        // routing chunks of a large call (rows of the per-chunk histogram)
 constexpr int kMinBM = 16;             // smallest token block of any tile config
 constexpr int kMaxBM = 128;            // largest token block (h rows are padded by this)
 constexpr int kNumBarriers = 6;
@@ -53,7 +52,6 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
   size_t ctrl, bars, counts, offsets, hist, r2s, s2r, h, h_sf, o, xsg, hsg, total;
-  int64_t chunk_slots;   // slots per routing chunk
   int64_t max_slots;     // max_tokens * k
   int64_t h_rows;        // rows of h (max_slots + kMaxBM padding)
   int64_t h_row_bytes, h_sf_row_bytes, o_row_bytes;
@@ -64,9 +62,6 @@ inline Layout make_layout(int64_t max_tokens, int64_t H, int64_t I, int64_t E, i
   Layout L{};
   const size_t A = 256;
   L.max_slots = max_tokens * k;
-  int64_t per = (L.max_slots + kMaxChunks - 1) / kMaxChunks;
-  L.chunk_slots = per <= kMinChunkSlots ? kMinChunkSlots
-                                        : (per + kMinChunkSlots - 1) / kMinChunkSlots * kMinChunkSlots;
   L.h_rows = L.max_slots + kMaxBM;
   L.h_row_bytes = recipe == 0 ? I * 2 : I;
   L.h_sf_row_bytes = recipe == 0 ? 0 : I / 32;
