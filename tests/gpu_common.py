@@ -213,6 +213,14 @@ def h_values(p: dict, codes: np.ndarray, sfs: np.ndarray) -> np.ndarray:
     return e4[codes] * np.repeat(np.ldexp(1.0, sfs.astype(np.int32) - 127), 32)
 
 
+def _b128_codes(h: np.ndarray) -> np.ndarray:
+    """e4m3 code values of a row re-quantised with one fp32 factor per 128
+    values: s = max(amax / 448, 2^-126), and the largest value is 448 * s."""
+    b = h.reshape(-1, 128)
+    s = np.maximum(np.abs(b).max(axis=1, keepdims=True) / 448.0, 2.0 ** -126)
+    return (b / s).reshape(-1)
+
+
 def scan_flips(p: dict, toks, s2r: np.ndarray, codes: np.ndarray, sfs: np.ndarray, hq: np.ndarray,
                delta: np.ndarray) -> tuple[np.ndarray, dict]:
     """Compare the GPU's re-quantised rows with the oracle's, for every valid
@@ -222,15 +230,18 @@ def scan_flips(p: dict, toks, s2r: np.ndarray, codes: np.ndarray, sfs: np.ndarra
     allowance on y that the differing values can cause,
         allow[q, n] = sum_j |w[t, j]| * sum_i |h_gpu - h_ref|_i * |W2(e_j, n, i)|
     (summed per expert as one product of |W2(e)| with the rows' differences),
-    and counts: rows, re-quantisation flips (a code that changed: more than
-    2^-16 of the value apart, finer than any e4m3 step; the fp32-scale recipe
-    also moves every value of a block by its scale's last bits) and the
-    32-element blocks holding one."""
+    and counts: rows, re-quantisation flips (an e4m3 code that changed) and
+    the 32-element blocks holding one.  With e8m0 scales a changed code shows
+    as a value more than 2^-16 apart, finer than any e4m3 step; with one fp32
+    factor per 128 values the factor's last bits move every value of a block,
+    so there the codes are compared: the block's largest value always holds
+    code 448, which gives the factor back exactly (code * s / s is exact)."""
     k, H, E = p["k"], p["H"], p["E"]
     idx, w = p["topk_idx"], p["topk_weights"]
     allow = np.zeros((len(toks), H), np.float64)
     per_expert = {}
-    flips = blocks = nrows = 0
+    flips = blocks = nrows = scale_moved = 0
+    scale_rel = 0.0
     n = 0
     for q, t in enumerate(toks):
         for j in range(k):
@@ -245,7 +256,15 @@ def scan_flips(p: dict, toks, s2r: np.ndarray, codes: np.ndarray, sfs: np.ndarra
                                    f"the rounding-decision band, first at i={np.where(bad)[0][:5]}")
             if np.any(d):
                 per_expert.setdefault(e, []).append((q, abs(float(w[t, j])), np.abs(d)))
-            flip = np.abs(d) > np.abs(hq[q, j]) * 2.0 ** -16
+            if p["recipe"] == synth.RECIPE_FP8_B128:
+                flip = _b128_codes(g) != _b128_codes(hq[q, j])
+                sg = np.abs(g.reshape(-1, 128)).max(axis=1)
+                sr = np.abs(hq[q, j].reshape(-1, 128)).max(axis=1)
+                rel = np.abs(sg - sr) / np.maximum(sr, 2.0 ** -126)
+                scale_moved += int((rel > 2.0 ** -16).sum())
+                scale_rel = max(scale_rel, float(rel.max()))
+            else:
+                flip = np.abs(d) > np.abs(hq[q, j]) * 2.0 ** -16
             flips += int(flip.sum())
             blocks += int(np.unique(np.nonzero(flip)[0] // 32).size)
             nrows += 1
@@ -256,7 +275,10 @@ def scan_flips(p: dict, toks, s2r: np.ndarray, codes: np.ndarray, sfs: np.ndarra
         contrib = w2_abs_cols(p, e, cols) @ D[cols]                    # [H, rows]
         for c, (q, wt, _) in enumerate(items):
             allow[q] += wt * contrib[:, c]
-    return allow, {"rows": nrows, "flips": flips, "flip_blocks": blocks}
+    stats = {"rows": nrows, "flips": flips, "flip_blocks": blocks}
+    if p["recipe"] == synth.RECIPE_FP8_B128:
+        stats.update(scale_moved_blocks=scale_moved, max_scale_rel=scale_rel)
+    return allow, stats
 
 
 def _record(stats: dict) -> None:
@@ -311,6 +333,9 @@ def check_collected(p: dict, toks, col: dict, what: str, clamp: float | None = N
     stats = {"what": what, "tokens": len(toks), "rows": fl["rows"], "flips": fl["flips"],
              "flip_blocks": fl["flip_blocks"], "raw_fp32": raw, "beyond_tol_fp32": over,
              "max_allow_over_rms": float(allow.max() / rms) if rms > 0 else 0.0, "elements": int(d.size)}
+    for key in ("scale_moved_blocks", "max_scale_rel"):
+        if key in fl:
+            stats[key] = fl[key]
     if "y16" in col:
         assert col["status16"] == status, f"{what}: device status {col['status16']} (bf16 y)"
         assert col["bf16_is_rounding"], f"{what}: bf16 y is not the rounding of the fp32 y"
@@ -322,6 +347,8 @@ def check_collected(p: dict, toks, col: dict, what: str, clamp: float | None = N
     log(f"  {what}: fp32 y max|dy|/rms = {raw:.3e}, beyond {TOL_FP8:g} rms: {over}/{d.size}; "
         f"{fl['flips']} flipped codes in {fl['flip_blocks']} blocks of {fl['rows']} rows "
         f"(max allowance/rms {stats['max_allow_over_rms']:.2e})"
+        + (f"; {fl['scale_moved_blocks']} 128-blocks whose scale moved by more than 2^-16 "
+           f"(max {fl['max_scale_rel']:.2e})" if "scale_moved_blocks" in fl else "")
         + (f"; bf16 y max|dy|/rms = {stats['raw_bf16']:.3e}, beyond: {stats['beyond_tol_bf16']}, "
            f"differing: {stats['differing_bf16']}" if "raw_bf16" in stats else ""))
     _record(stats)
