@@ -298,7 +298,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="deepseek_fp8xfp4_T8192_zipf")
     ap.add_argument("--secondary", default="deepseek_fp8xfp4_T128")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
