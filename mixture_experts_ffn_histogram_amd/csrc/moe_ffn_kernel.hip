@@ -667,11 +667,10 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
           const size_t row = (size_t)(row0 + m);
 #pragma unroll
           for (int hh = 0; hh < 2; hh++) {
-            uint32_t word = 0;
+            float q[4];
 #pragma unroll
-            for (int j = 0; j < 4; j++)
-              word |= f32_to_e4m3(swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp) / sc) << (8 * j);
-            stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
+            for (int j = 0; j < 4; j++) q[j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp) / sc;
+            stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), e4m3x4(q[0], q[1], q[2], q[3]));
           }
           if (wave == 0 && g == 0) stg4(p.h_sf + row * (size_t)(I / 32) + (size_t)nb * 4, __float_as_uint(sc));
         }
@@ -710,9 +709,8 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
         if (m < nrows) {
 #pragma unroll
           for (int hh = 0; hh < 2; hh++) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int j = 0; j < 4; j++) word |= f32_to_e4m3(__builtin_amdgcn_ldexpf(hv[hh * 4 + j], -E)) << (8 * j);
+            const uint32_t word = e4m3x4(__builtin_amdgcn_ldexpf(hv[hh * 4 + 0], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 1], -E),
+                                          __builtin_amdgcn_ldexpf(hv[hh * 4 + 2], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 3], -E));
             stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
           }
           if (g == 0) stg1(p.h_sf + row * (size_t)(I / 32) + (size_t)(i0 / 32), (uint8_t)(E + 127));
@@ -918,9 +916,8 @@ __device__ void wave_tile(const KParams& p, const Shared& sh, const int* lr2s, b
         if (m < nrows) {
 #pragma unroll
           for (int hh = 0; hh < 2; hh++) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int j = 0; j < 4; j++) word |= f32_to_e4m3(__builtin_amdgcn_ldexpf(hv[hh * 4 + j], -E)) << (8 * j);
+            const uint32_t word = e4m3x4(__builtin_amdgcn_ldexpf(hv[hh * 4 + 0], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 1], -E),
+                                          __builtin_amdgcn_ldexpf(hv[hh * 4 + 2], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 3], -E));
             stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
           }
           if (g == 0) stg1(p.h_sf + row * (size_t)(I / 32) + (size_t)(i0 / 32), (uint8_t)(E + 127));
@@ -1218,9 +1215,8 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
         const size_t row = (size_t)(row0 + m);
 #pragma unroll
         for (int hh = 0; hh < 2; hh++) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int j = 0; j < 4; j++) word |= f32_to_e4m3(__builtin_amdgcn_ldexpf(hv[hh * 4 + j], -E)) << (8 * j);
+          const uint32_t word = e4m3x4(__builtin_amdgcn_ldexpf(hv[hh * 4 + 0], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 1], -E),
+                                        __builtin_amdgcn_ldexpf(hv[hh * 4 + 2], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 3], -E));
           stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
         }
         if (g == 0) {
@@ -1457,9 +1453,8 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
         const size_t row = (size_t)(row0 + m);
 #pragma unroll
         for (int hh = 0; hh < 2; hh++) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int j = 0; j < 4; j++) word |= f32_to_e4m3(__builtin_amdgcn_ldexpf(hv[hh * 4 + j], -E)) << (8 * j);
+          const uint32_t word = e4m3x4(__builtin_amdgcn_ldexpf(hv[hh * 4 + 0], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 1], -E),
+                                        __builtin_amdgcn_ldexpf(hv[hh * 4 + 2], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 3], -E));
           stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
         }
         if (g == 0) stg1(p.h_sf + row * (size_t)(I / 32) + (size_t)(i0 / 32), (uint8_t)(E + 127));

@@ -58,12 +58,11 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_act_kernel(const uint1
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, 64));
       const int E = block_scale_exp(amax);
-      uint32_t lo = 0, hi = 0;
+      float g[8];
 #pragma unroll
-      for (int i = 0; i < 4; i++) {
-        lo |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[i], -E)) << (8 * i);
-        hi |= f32_to_e4m3(__builtin_amdgcn_ldexpf(f[4 + i], -E)) << (8 * i);
-      }
+      for (int i = 0; i < 8; i++) g[i] = __builtin_amdgcn_ldexpf(f[i], -E);  // |g| <= 448 by the choice of E
+      const uint32_t lo = e4m3x4(g[0], g[1], g[2], g[3]);
+      const uint32_t hi = e4m3x4(g[4], g[5], g[6], g[7]);
       if (in[u]) {
         stg8(q + e0, lo, hi);
         if ((lane & 3) == 0) stg1(sf + (e0 >> 5), (uint8_t)(E + 127));
