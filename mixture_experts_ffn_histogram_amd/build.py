@@ -45,20 +45,24 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     return LIB
 
 
-def build_test_helpers(verbose: bool = False) -> str:
-    """Compile the test-only side-stream helper (tests/native) for gfx950."""
+def build_test_helpers(verbose: bool = False) -> list:
+    """Compile the test-only helpers (tests/native) for gfx950: the side-stream
+    kernel and the e4m3 conversion check."""
     root = os.path.dirname(HERE)
-    src = os.path.join(root, "tests", "native", "side_kernel.hip")
-    out = os.path.join(root, "tests", "native", "libmoe_side.so")
-    cmd = [HIPCC] + COMMON + ["-shared", "-x", "hip", src, "-o", out + ".tmp"]
-    if verbose:
-        print(" ".join(cmd))
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed on the side-stream test helper")
-    os.replace(out + ".tmp", out)
-    return out
+    outs = []
+    for src_name, lib_name in (("side_kernel.hip", "libmoe_side.so"), ("e4m3_convert.hip", "libmoe_e4m3.so")):
+        src = os.path.join(root, "tests", "native", src_name)
+        out = os.path.join(root, "tests", "native", lib_name)
+        cmd = [HIPCC] + COMMON + ["-shared", "-x", "hip", src, "-o", out + ".tmp"]
+        if verbose:
+            print(" ".join(cmd))
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stdout + r.stderr)
+            raise RuntimeError(f"hipcc failed on the test helper {src_name}")
+        os.replace(out + ".tmp", out)
+        outs.append(out)
+    return outs
 
 
 if __name__ == "__main__":

@@ -1,0 +1,60 @@
+"""The forward's packed e4m3 conversion against the oracle's encoder (MI355X only).
+
+The L1 epilogues and the pre-dispatch quantiser write their e4m3 codes with
+the hardware pack conversion (`e4m3x4` in the device helpers).  Its codes
+must be the oracle's (its round-to-nearest-even saturating rounding, then its
+encoder) for every
+value the kernels can hand it: every e4m3 value, every midpoint between
+neighbouring values and the floats next to it, fp32 denormals, magnitudes in
+(448, 464] (the fp32-scale recipe's quotient can pass 448 by an ulp), and
+random values over the whole range, uniform and log-uniform."""
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def conversion_inputs() -> np.ndarray:
+    pos = sorted({oracle.dec_e4m3(c) for c in range(0x7F)})           # 0 .. 448, finite codes
+    vals = [v for p in pos for v in (p, -p)]
+    for a, b in zip(pos[:-1], pos[1:]):
+        mid = np.float32(0.5 * (a + b))                                # exact: neighbours differ in 4 bits
+        for m in (mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1e30))):
+            vals += [float(m), -float(m)]
+    vals += list(np.arange(1, 65, dtype=np.uint32).view(np.float32) * 1)   # fp32 denormals
+    vals += [448.0 + 0.5 * k for k in range(1, 33)] + [-(448.0 + 0.5 * k) for k in range(1, 33)]
+    vals.append(float(np.nextafter(np.float32(448), np.float32(1e30))))
+    rng = np.random.default_rng(2024)
+    uni = rng.uniform(-448.0, 448.0, 100_000).astype(np.float32)
+    log = (np.exp2(rng.uniform(-30.0, 8.7, 100_000)) * rng.choice([-1.0, 1.0], 100_000)).astype(np.float32)
+    v = np.concatenate([np.asarray(vals, np.float32), uni, log])
+    pad = (-v.size) % 4
+    return np.concatenate([v, np.zeros(pad, np.float32)])
+
+
+def test_e4m3x4_matches_oracle_encoder():
+    path = os.path.join(HERE, "native", "libmoe_e4m3.so")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} is missing: build it with mixture_experts_ffn_histogram_amd/build.py build_test_helpers()")
+    lib = ctypes.CDLL(path)
+    lib.moe_test_e4m3x4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.moe_test_e4m3x4.restype = ctypes.c_int
+    v = conversion_inputs()
+    n4 = v.size // 4
+    x = torch.from_numpy(v).cuda()
+    out = torch.zeros(n4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    assert lib.moe_test_e4m3x4(x.data_ptr(), out.data_ptr(), n4, stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint8)                             # byte j of dword i = value 4 i + j
+    ref = np.fromiter((oracle.enc_e4m3(oracle.round_e4m3_sat(float(a))) for a in v), np.uint8, count=v.size)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (f"{bad.size} of {v.size} codes differ, first: "
+                           + ", ".join(f"{v[i]!r}: gpu 0x{got[i]:02x} oracle 0x{ref[i]:02x}" for i in bad[:6]))
