@@ -1100,9 +1100,11 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
       compute(u, u);
     }
   }
-  // every wave is done with the ring before the next tile refills it
+  // every wave is done with the ring before the next tile refills it or the
+  // L2 epilogue writes into it (a full workgroup barrier: its fences keep the
+  // compiler from moving LDS accesses across it)
   MOEFFN_WAIT_VMCNT(0);
-  __builtin_amdgcn_s_barrier();
+  __syncthreads();
 }
 
 // One 128-row tile: expert e, token block mb, feature block nb (L1: 128
@@ -1194,7 +1196,6 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_full, as_last, sa_base, rX, xoff, brd0, brd1,
                 rXs, xs_off, (uint32_t)p.sg_rows * 4u, nk, wave, lane);
 
-  if (!active) return;
   if (l1) {
     const int i0 = rb[0];
 #pragma unroll
@@ -1227,13 +1228,30 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
       }
     }
   } else {
+    // o through LDS, one 16-row block t at a time (the ring buffers are free:
+    // the K loop ends on a barrier): the waves' 16 x 64 values go to buffer
+    // t % 3 as [row][256 outputs] (row stride 1 KB + 16 bytes), then each
+    // wave stores 4 whole rows of the tile's 256 outputs, 1 KB contiguous per
+    // instruction (8 whole cache lines instead of 64-byte pieces of 16 rows).
+    // A buffer is written again three blocks later, after two more barriers
+    // that every wave reaches only once done reading it.  Waves whose rows
+    // lie past H (the last block of an odd H/128) write nothing but store the
+    // other waves' outputs.
+    constexpr int kOStride = 1040;
+    const int c0 = nb * 256 + lane * 4;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      const int m = t * 16 + r16;
-      if (m < nrows) {
-        const size_t row = (size_t)(row0 + m);
+      uint8_t* bp = t % 3 == 0 ? R.b0 : t % 3 == 1 ? R.b1 : R.b2;
+      if (active) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) stg16f(p.o + row * H + (size_t)(rb[j] + 4 * g), acc[j][t]);
+        for (int j = 0; j < 4; j++) *(v4f*)(bp + r16 * kOStride + (wave * 64 + 16 * j + 4 * g) * 4) = acc[j][t];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int rr = 0; rr < 4; rr++) {
+        const int m = t * 16 + wave * 4 + rr;
+        const v4f v = *(const v4f*)(bp + (wave * 4 + rr) * kOStride + lane * 16);
+        if (m < nrows && c0 < H) stg16f(p.o + (size_t)(row0 + m) * H + (size_t)c0, v);
       }
     }
   }
