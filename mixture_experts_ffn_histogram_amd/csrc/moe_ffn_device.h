@@ -29,6 +29,7 @@ __device__ __forceinline__ v4i ldg16_nt(const void* p) { return __builtin_nontem
 __device__ __forceinline__ uint32_t ldg4(const void* p) { return *(gu32_c*)p; }
 __device__ __forceinline__ v4f ldg16f(const void* p) { return *(gv4f_c*)p; }
 __device__ __forceinline__ void stg16f(void* p, v4f v) { *(gv4f*)p = v; }
+__device__ __forceinline__ void stg16(void* p, v4i v) { *(gv4i*)p = v; }
 __device__ __forceinline__ void stg4(void* p, uint32_t v) { *(gu32*)p = v; }
 __device__ __forceinline__ void stg1(void* p, uint8_t v) { *(gu8*)p = v; }
 __device__ __forceinline__ void stg8(void* p, uint32_t lo, uint32_t hi) { *(gu64*)p = ((uint64_t)hi << 32) | lo; }

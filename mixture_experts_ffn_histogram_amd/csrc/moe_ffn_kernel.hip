@@ -1197,7 +1197,15 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
                 rXs, xs_off, (uint32_t)p.sg_rows * 4u, nk, wave, lane);
 
   if (l1) {
-    const int i0 = rb[0];
+    // h through LDS (the ring buffers are free: the K loop ends on a
+    // barrier): the tile's 128 rows x 128 code bytes go to buffer 0 (row
+    // stride 144 bytes: the 4-byte writes of a wave hit 64 distinct banks),
+    // the four 1x32 scale bytes of each row to buffer 1 as one dword (byte
+    // `wave` = block 4 nb + wave); then the tile leaves as whole 128-byte rows
+    // of h and one dword per row of h_sf and of the stage-major copy hsg.
+    constexpr int kHStride = 144;
+    uint8_t* hb = R.b0;
+    uint8_t* sfb = R.b1;
 #pragma unroll
     for (int t = 0; t < NT; t++) {
       const int m = t * 16 + r16;
@@ -1212,20 +1220,24 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
       amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
       const int E = block_scale_exp(amax);
-      if (m < nrows) {
-        const size_t row = (size_t)(row0 + m);
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-          const uint32_t word = e4m3x4(__builtin_amdgcn_ldexpf(hv[hh * 4 + 0], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 1], -E),
-                                        __builtin_amdgcn_ldexpf(hv[hh * 4 + 2], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 3], -E));
-          stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), word);
-        }
-        if (g == 0) {
-          stg1(p.h_sf + row * (size_t)(I / 32) + (size_t)(i0 / 32), (uint8_t)(E + 127));
-          // byte `wave` of stage nb's dword of the row (block i0/32 = 4 nb + wave)
-          stg1(reinterpret_cast<uint8_t*>(p.hsg + (size_t)nb * p.sg_rows + row) + wave, (uint8_t)(E + 127));
-        }
-      }
+      for (int hh = 0; hh < 2; hh++)
+        *(uint32_t*)(hb + m * kHStride + wave * 32 + hh * 16 + 4 * g) =
+            e4m3x4(__builtin_amdgcn_ldexpf(hv[hh * 4 + 0], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 1], -E),
+                   __builtin_amdgcn_ldexpf(hv[hh * 4 + 2], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 3], -E));
+      if (g == 0) sfb[m * 4 + wave] = (uint8_t)(E + 127);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int k = 0; k < 4; k++) {  // 1024 pieces of 16 bytes: row piece / 8, chunk piece % 8
+      const int piece = k * kThreads + tid, r = piece >> 3, c = piece & 7;
+      if (r < nrows)
+        stg16(p.h + (size_t)(row0 + r) * I + (size_t)(nb * 128 + c * 16), *(const v4i*)(hb + r * kHStride + c * 16));
+    }
+    if (tid < nrows) {
+      const uint32_t sw = *(const uint32_t*)(sfb + tid * 4);
+      stg4(p.h_sf + (size_t)(row0 + tid) * (size_t)(I / 32) + (size_t)nb * 4, sw);
+      stg4(p.hsg + (size_t)nb * p.sg_rows + (size_t)(row0 + tid), sw);
     }
   } else {
     // o through LDS, one 16-row block t at a time (the ring buffers are free:
