@@ -1663,22 +1663,78 @@ __device__ __forceinline__ void phase_big_tiles(const KParams& p, Shared& sh, co
 // ---------------------------------------------------------------------------
 // C: combine.  A unit of work is one token x 1024 columns (units spread
 // evenly over the waves even when T is not a multiple of the wave count): the
-// wave reads the token's k row indices and weights, then streams the k fp32
-// rows of o in 256-column slices (64 lanes x 4 floats), two slices in flight,
-// accumulating in slot order j = 0..k-1 with fused multiply-adds.
+// wave holds the token's k row indices and weights in lanes 0..k-1 (those of
+// its first unit loaded before the barrier that ends the L2 phase: routing is
+// final long before), then streams the k fp32 rows of o in 256-column slices
+// (64 lanes x 4 floats) and sums in slot order j = 0..k-1 with fused
+// multiply-adds.  WIDE (the kernels with registers to spare): with k <= 8 all
+// 4 slices of all slots are in flight at once; else two slices of 8 slots.
 // ---------------------------------------------------------------------------
-__device__ void phase_combine(const KParams& p) {
+__device__ __forceinline__ void combine_first_meta(const KParams& p, int& myrow, float& myw) {
+  const int lane = threadIdx.x & 63;
+  const int nc = (p.H + 1023) >> 10;
+  const int u = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const bool has = u < p.T * nc && lane < p.k;
+  myrow = has ? p.s2r[(size_t)(u / nc) * p.k + lane] : -1;
+  myw = has ? p.tw[(size_t)(u / nc) * p.k + lane] : 0.f;
+}
+
+__device__ __forceinline__ void combine_store(const KParams& p, int t, int c, const v4f& a) {
+  if (p.y_fp32) {
+    stg16f((float*)p.y + (size_t)t * p.H + c, a);
+  } else {
+    stg8((uint16_t*)p.y + (size_t)t * p.H + c, f32_to_bf16(a[0]) | (f32_to_bf16(a[1]) << 16),
+         f32_to_bf16(a[2]) | (f32_to_bf16(a[3]) << 16));
+  }
+}
+
+template <bool WIDE>
+__device__ void phase_combine(const KParams& p, int myrow, float myw) {
   const int lane = threadIdx.x & 63;
   const int H = p.H, k = p.k;
   const int nw = gridDim.x * 4;
   const int nc = (H + 1023) >> 10;  // 1024-column units per token
   const int units = p.T * nc;
-  for (int u = blockIdx.x * 4 + (threadIdx.x >> 6); u < units; u += nw) {
+  const int u0 = blockIdx.x * 4 + (threadIdx.x >> 6);
+  for (int u = u0; u < units; u += nw) {
     const int t = u / nc, cu = u - t * nc;
-    // lane j < k holds slot j's row and weight
-    const int myrow = lane < k ? p.s2r[(size_t)t * k + lane] : -1;
-    const float myw = lane < k ? p.tw[(size_t)t * k + lane] : 0.f;
+    if (u != u0) {  // lane j < k holds slot j's row and weight
+      myrow = lane < k ? p.s2r[(size_t)t * k + lane] : -1;
+      myw = lane < k ? p.tw[(size_t)t * k + lane] : 0.f;
+    }
     const int cend = min(H, (cu + 1) << 10);
+    if constexpr (WIDE) {
+      if (k <= 8) {
+        int rows[8];
+        float ws[8];
+        v4f ov[8][4];
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          rows[j] = j < k ? __shfl(myrow, j, 64) : -1;
+          ws[j] = j < k ? __shfl(myw, j, 64) : 0.f;
+          const size_t base = (size_t)(rows[j] < 0 ? 0 : rows[j]) * H;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const int c = (cu << 10) + q * 256 + lane * 4;
+            ov[j][q] = (rows[j] >= 0 && c < cend) ? ldg16f(p.o + base + c) : v4f{0.f, 0.f, 0.f, 0.f};
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          v4f a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 8; j++) {
+            if (rows[j] >= 0) {
+#pragma unroll
+              for (int c = 0; c < 4; c++) a[c] = __builtin_fmaf(ws[j], ov[j][q][c], a[c]);
+            }
+          }
+          const int c = (cu << 10) + q * 256 + lane * 4;
+          if (c < cend) combine_store(p, t, c, a);
+        }
+        continue;
+      }
+    }
     for (int c0 = cu << 10; c0 < cend; c0 += 512) {
       const int ca = c0 + lane * 4;
       const int cb = c0 + 256 + lane * 4;
@@ -1708,15 +1764,8 @@ __device__ void phase_combine(const KParams& p) {
           }
         }
       }
-      if (p.y_fp32) {
-        if (va) stg16f((float*)p.y + (size_t)t * H + ca, acca);
-        if (vb) stg16f((float*)p.y + (size_t)t * H + cb, accb);
-      } else {
-        if (va) stg8((uint16_t*)p.y + (size_t)t * H + ca, f32_to_bf16(acca[0]) | (f32_to_bf16(acca[1]) << 16),
-                     f32_to_bf16(acca[2]) | (f32_to_bf16(acca[3]) << 16));
-        if (vb) stg8((uint16_t*)p.y + (size_t)t * H + cb, f32_to_bf16(accb[0]) | (f32_to_bf16(accb[1]) << 16),
-                     f32_to_bf16(accb[2]) | (f32_to_bf16(accb[3]) << 16));
-      }
+      if (va) combine_store(p, t, ca, acca);
+      if (vb) combine_store(p, t, cb, accb);
     }
   }
 }
@@ -1757,8 +1806,13 @@ __device__ __forceinline__ void run_call(const KParams& p, Shared& sh, WaveCount
     if constexpr (kBig) phase_big_tiles<RECIPE>(p, sh, *big, false);
     else if constexpr (BM <= 32) phase_wave_tiles<RECIPE, BM, TILED>(p, sh, lr2s, local, false);
     else phase_wg_tiles<RECIPE, BM, TILED>(p, sh, *sb, lr2s, local, false);
-    if (!grid_barrier(p, BAR_L2, local ? 1 : 3, sh)) goto done;
-    phase_combine(p);
+    {
+      int crow;
+      float cw;
+      combine_first_meta(p, crow, cw);
+      if (!grid_barrier(p, BAR_L2, local ? 1 : 3, sh)) goto done;
+      phase_combine<!kBig>(p, crow, cw);
+    }
   }
 done:
   fence_release();
