@@ -261,7 +261,8 @@ int moe_ffn_launch_size(int physical_cus, int reserved_cus, int max_cus);
 
 /* Byte offsets of the intermediates inside the workspace, for inspection:
    h ([max_tokens*k + pad, I] e4m3, or bf16), h_sf ([.., I/32] e8m0) and
-   o ([max_tokens*k, H] fp32 per routed row). */
+   o ([max_tokens*k, H] per routed row: the L2 result in bf16 for the e4m3
+   recipes, in fp32 for the BF16 recipe; o_row_bytes gives which). */
 typedef struct {
     size_t h, h_sf, o;
     int64_t h_row_bytes, h_sf_row_bytes, o_row_bytes;

@@ -284,7 +284,7 @@ int forward_enqueue(const moe_ffn_problem* p, const moe_ffn_args* a, void* works
   k.s2r = reinterpret_cast<int32_t*>(ws + L.s2r);
   k.h = ws + L.h;
   k.h_sf = ws + L.h_sf;
-  k.o = reinterpret_cast<float*>(ws + L.o);
+  k.o = ws + L.o;
 
   int bm = choose_block_m(recipe, T, p->top_k, p->num_experts);
   const long bm_env = env_long("MOE_FFN_BLOCK_M", 0);  // tuning override: 16, 32, 64 or 128

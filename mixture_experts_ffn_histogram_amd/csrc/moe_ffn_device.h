@@ -90,6 +90,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Two values to bf16 bits packed into a dword (low half = a) with the
+// hardware pack conversion, round to nearest even (fp32 denormals kept).
+typedef __bf16 moe_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float moe_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(moe_f32x2{a, b}, moe_bf16x2));
+}
+
 // Exponent E of the e8m0 scale of a 1x32 block: the smallest integer with
 // amax <= 448 * 2^E (448 = 1.75 * 2^8), clamped to [-127, 127]; 0 for an
 // all-zero block.  Exact on the fp32 bit pattern: with amax = f * 2^p,

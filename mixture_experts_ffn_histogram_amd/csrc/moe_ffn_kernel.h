@@ -50,7 +50,7 @@ struct KParams {
   int32_t* s2r;
   uint8_t* h;
   uint8_t* h_sf;
-  float* o;
+  void* o;                 // per routed row: H fp32 values (BF16 recipe) or H bf16 values (e4m3 recipes)
   // 128-row tiles only (else null): stage-major scale copies, sg_rows rows each
   uint32_t* xsg;
   uint32_t* hsg;

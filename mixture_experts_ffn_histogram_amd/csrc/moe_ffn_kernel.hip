@@ -94,6 +94,18 @@ struct SharedB {
   uint32_t bsfoff[BM];   // byte offset of its scale row
 };
 
+// Four consecutive values of a routed row's L2 result (element index idx of
+// the [rows][H] buffer): fp32 for the BF16 recipe; bf16, rounded to nearest
+// even, for the e4m3 recipes (the output type; the combine sums in fp32).
+template <int RECIPE>
+__device__ __forceinline__ void store_o4(const KParams& p, size_t idx, const v4f& v) {
+  if constexpr (RECIPE == 0) {
+    stg16f((float*)p.o + idx, v);
+  } else {
+    stg8((uint16_t*)p.o + idx, bf16x2(v[0], v[1]), bf16x2(v[2], v[3]));
+  }
+}
+
 // Slot of routed row `row`: from LDS for a small call, else from the workspace.
 __device__ __forceinline__ int route_slot(const KParams& p, const int* lr2s, bool local, int row) {
   return local ? lr2s[row] : (int)ldg4(p.r2s + row);
@@ -724,7 +736,7 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
       if (m < nrows) {
         const size_t row = (size_t)(row0 + m);
 #pragma unroll
-        for (int j = 0; j < 4; j++) stg16f(p.o + row * H + (size_t)(arow[j] + 4 * g), acc[j][t]);
+        for (int j = 0; j < 4; j++) store_o4<RECIPE>(p, row * H + (size_t)(arow[j] + 4 * g), acc[j][t]);
       }
     }
   }
@@ -931,7 +943,7 @@ __device__ void wave_tile(const KParams& p, const Shared& sh, const int* lr2s, b
       if (m < nrows) {
         const size_t row = (size_t)(row0 + m);
 #pragma unroll
-        for (int j = 0; j < 4; j++) stg16f(p.o + row * H + (size_t)(arow[j] + 4 * g), acc[j][t]);
+        for (int j = 0; j < 4; j++) store_o4<RECIPE>(p, row * H + (size_t)(arow[j] + 4 * g), acc[j][t]);
       }
     }
   }
@@ -1263,7 +1275,7 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
       for (int rr = 0; rr < 4; rr++) {
         const int m = t * 16 + wave * 4 + rr;
         const v4f v = *(const v4f*)(bp + (wave * 4 + rr) * kOStride + lane * 16);
-        if (m < nrows && c0 < H) stg16f(p.o + (size_t)(row0 + m) * H + (size_t)c0, v);
+        if (m < nrows && c0 < H) store_o4<RECIPE>(p, (size_t)(row0 + m) * H + (size_t)c0, v);
       }
     }
   }
@@ -1497,7 +1509,7 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
       if (m < nrows) {
         const size_t row = (size_t)(row0 + m);
 #pragma unroll
-        for (int j = 0; j < 4; j++) stg16f(p.o + row * H + (size_t)(rb[j] + 4 * g), acc[j][t]);
+        for (int j = 0; j < 4; j++) store_o4<2>(p, row * H + (size_t)(rb[j] + 4 * g), acc[j][t]);
       }
     }
   }
@@ -1665,10 +1677,13 @@ __device__ __forceinline__ void phase_big_tiles(const KParams& p, Shared& sh, co
 // evenly over the waves even when T is not a multiple of the wave count): the
 // wave holds the token's k row indices and weights in lanes 0..k-1 (those of
 // its first unit loaded before the barrier that ends the L2 phase: routing is
-// final long before), then streams the k fp32 rows of o in 256-column slices
-// (64 lanes x 4 floats) and sums in slot order j = 0..k-1 with fused
-// multiply-adds.  WIDE (the kernels with registers to spare): with k <= 8 all
-// 4 slices of all slots are in flight at once; else two slices of 8 slots.
+// final long before), then streams the k rows of o and sums in slot order
+// j = 0..k-1 with fused multiply-adds in fp32.  bf16 rows (e4m3 recipes): a
+// lane takes 8 columns of each 512-column half, so one unit is two 16-byte
+// loads per slot, all of them for 8 slots in flight at once.  fp32 rows (BF16
+// recipe): 256-column slices of 64 lanes x 4 floats; WIDE (the kernels with
+// registers to spare): with k <= 8 all 4 slices of all slots in flight at
+// once; else two slices of 8 slots.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void combine_first_meta(const KParams& p, int& myrow, float& myw) {
   const int lane = threadIdx.x & 63;
@@ -1688,8 +1703,80 @@ __device__ __forceinline__ void combine_store(const KParams& p, int t, int c, co
   }
 }
 
-template <bool WIDE>
+// Eight consecutive outputs y[t, c .. c+7] from fp32 sums.
+__device__ __forceinline__ void combine_store8(const KParams& p, int t, int c, const float* a) {
+  if (p.y_fp32) {
+    stg16f((float*)p.y + (size_t)t * p.H + c, v4f{a[0], a[1], a[2], a[3]});
+    stg16f((float*)p.y + (size_t)t * p.H + c + 4, v4f{a[4], a[5], a[6], a[7]});
+  } else {
+    v4i w;
+#pragma unroll
+    for (int i = 0; i < 4; i++) w[i] = (int)(f32_to_bf16(a[2 * i]) | (f32_to_bf16(a[2 * i + 1]) << 16));
+    stg16((uint16_t*)p.y + (size_t)t * p.H + c, w);
+  }
+}
+
+// bf16 rows of o (e4m3 recipes).  H is a multiple of 32, so no 8-column
+// piece straddles the end of a row.
+__device__ void phase_combine_b16(const KParams& p, int myrow, float myw) {
+  const int lane = threadIdx.x & 63;
+  const int H = p.H, k = p.k;
+  const int nw = gridDim.x * 4;
+  const int nc = (H + 1023) >> 10;  // 1024-column units per token
+  const int units = p.T * nc;
+  const int u0 = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const uint16_t* o = (const uint16_t*)p.o;
+  for (int u = u0; u < units; u += nw) {
+    const int t = u / nc, cu = u - t * nc;
+    if (u != u0) {  // lane j < k holds slot j's row and weight
+      myrow = lane < k ? p.s2r[(size_t)t * k + lane] : -1;
+      myw = lane < k ? p.tw[(size_t)t * k + lane] : 0.f;
+    }
+    const int cend = min(H, (cu + 1) << 10);
+    const int ca = (cu << 10) + lane * 8, cb = ca + 512;
+    const bool va = ca < cend, vb = cb < cend;
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) acc[i] = 0.f;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      v4i oa[8], ob[8];
+      int rows[8];
+      float ws[8];
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int jj = j0 + j;
+        rows[j] = jj < k ? __shfl(myrow, jj, 64) : -1;
+        ws[j] = jj < k ? __shfl(myw, jj, 64) : 0.f;
+        const size_t base = (size_t)(rows[j] < 0 ? 0 : rows[j]) * H;
+        oa[j] = (rows[j] >= 0 && va) ? ldg16(o + base + ca) : v4i{0, 0, 0, 0};
+        ob[j] = (rows[j] >= 0 && vb) ? ldg16(o + base + cb) : v4i{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        if (rows[j] >= 0) {
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            const uint32_t a = (uint32_t)oa[j][c], b = (uint32_t)ob[j][c];
+            acc[2 * c] = __builtin_fmaf(ws[j], __uint_as_float(a << 16), acc[2 * c]);
+            acc[2 * c + 1] = __builtin_fmaf(ws[j], __uint_as_float(a & 0xFFFF0000u), acc[2 * c + 1]);
+            acc[8 + 2 * c] = __builtin_fmaf(ws[j], __uint_as_float(b << 16), acc[8 + 2 * c]);
+            acc[8 + 2 * c + 1] = __builtin_fmaf(ws[j], __uint_as_float(b & 0xFFFF0000u), acc[8 + 2 * c + 1]);
+          }
+        }
+      }
+    }
+    if (va) combine_store8(p, t, ca, acc);
+    if (vb) combine_store8(p, t, cb, acc + 8);
+  }
+}
+
+template <int RECIPE, bool WIDE>
 __device__ void phase_combine(const KParams& p, int myrow, float myw) {
+  if constexpr (RECIPE != 0) {
+    phase_combine_b16(p, myrow, myw);
+    return;
+  }
+  const float* o = (const float*)p.o;
   const int lane = threadIdx.x & 63;
   const int H = p.H, k = p.k;
   const int nw = gridDim.x * 4;
@@ -1716,7 +1803,7 @@ __device__ void phase_combine(const KParams& p, int myrow, float myw) {
 #pragma unroll
           for (int q = 0; q < 4; q++) {
             const int c = (cu << 10) + q * 256 + lane * 4;
-            ov[j][q] = (rows[j] >= 0 && c < cend) ? ldg16f(p.o + base + c) : v4f{0.f, 0.f, 0.f, 0.f};
+            ov[j][q] = (rows[j] >= 0 && c < cend) ? ldg16f(o + base + c) : v4f{0.f, 0.f, 0.f, 0.f};
           }
         }
 #pragma unroll
@@ -1750,8 +1837,8 @@ __device__ void phase_combine(const KParams& p, int myrow, float myw) {
           rows[j] = jj < k ? __shfl(myrow, jj, 64) : -1;
           ws[j] = jj < k ? __shfl(myw, jj, 64) : 0.f;
           const size_t base = (size_t)(rows[j] < 0 ? 0 : rows[j]) * H;
-          oa[j] = (rows[j] >= 0 && va) ? ldg16f(p.o + base + ca) : v4f{0.f, 0.f, 0.f, 0.f};
-          ob[j] = (rows[j] >= 0 && vb) ? ldg16f(p.o + base + cb) : v4f{0.f, 0.f, 0.f, 0.f};
+          oa[j] = (rows[j] >= 0 && va) ? ldg16f(o + base + ca) : v4f{0.f, 0.f, 0.f, 0.f};
+          ob[j] = (rows[j] >= 0 && vb) ? ldg16f(o + base + cb) : v4f{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int j = 0; j < 8; j++) {
@@ -1811,7 +1898,7 @@ __device__ __forceinline__ void run_call(const KParams& p, Shared& sh, WaveCount
       float cw;
       combine_first_meta(p, crow, cw);
       if (!grid_barrier(p, BAR_L2, local ? 1 : 3, sh)) goto done;
-      phase_combine<!kBig>(p, crow, cw);
+      phase_combine<RECIPE, !kBig>(p, crow, cw);
     }
   }
 done:

@@ -65,7 +65,7 @@ inline Layout make_layout(int64_t max_tokens, int64_t H, int64_t I, int64_t E, i
   L.h_rows = L.max_slots + kMaxBM;
   L.h_row_bytes = recipe == 0 ? I * 2 : I;
   L.h_sf_row_bytes = recipe == 0 ? 0 : I / 32;
-  L.o_row_bytes = H * 4;
+  L.o_row_bytes = recipe == 0 ? H * 4 : H * 2;  // the L2 result per routed row: fp32 / bf16
   size_t off = 0;
   L.ctrl = off;    off = align_up(off + sizeof(Ctrl), A);
   L.bars = off;    off = align_up(off + kBarRegionBytes, A);

@@ -70,8 +70,8 @@ def lib():
             ("oracle_forward", ctypes.c_int, [P] + [P] * 14),
             ("oracle_forward_tokens", ctypes.c_int, [P] + [P] * 8 + [P, i64, P]),
             ("oracle_forward_tokens_band", ctypes.c_int, [P] + [P] * 8 + [P, i64, P, d, P]),
-            ("oracle_forward_tokens_rows", ctypes.c_int, [P] + [P] * 8 + [P, i64, P, d, P, P]),
-            ("oracle_ffn_row", ctypes.c_int, [P, P, P, i64, i64, P, P, P, P, P, P, P, P, P, P, d, P]),
+            ("oracle_forward_tokens_rows", ctypes.c_int, [P] + [P] * 8 + [P, i64, P, d, P, P, P, P]),
+            ("oracle_ffn_row", ctypes.c_int, [P, P, P, i64, i64, P, P, P, P, P, P, P, P, P, P, d, P, P, P]),
             ("oracle_num_threads", ctypes.c_int, []),
             ("oracle_quantize_act", ctypes.c_int, [P, i64, i64, P, P]),
             ("oracle_route_topk", ctypes.c_int, [P, P, i64, i64, i64, i64, P, P, P]),
@@ -132,7 +132,8 @@ def forward(p: dict, y_fp32: bool, clamp: float, want_tables: bool = False, want
     """Full routed forward.  ``p`` holds the problem arrays (see the synth module).
 
     Returns y (float32 array, or uint16 bf16 bits when y_fp32 is False) and,
-    on request, the routing tables and the per-row fp32 L2 outputs.
+    on request, the routing tables and the per-row L2 outputs (float32 arrays; bf16 values for the
+    e4m3 recipes).
     """
     T, H, I, E, k, recipe = p["T"], p["H"], p["I"], p["E"], p["k"], p["recipe"]
     x, x_sf, idx, w, w1, w1_sf, w2, w2_sf = _args(p)
@@ -198,26 +199,33 @@ def forward_tokens_rows(p: dict, tokens, y_fp32: bool, clamp: float, rho: float)
     """Per-token forward of the listed tokens that also returns, for every slot
     j of listed token q, the re-quantised activation values of that routed row
     (hq[q, j, :]) and the rounding-decision band of each for `rho`
-    (delta[q, j, :]); masked slots keep NaN rows.  Returns (y_rows, hq, delta,
-    status)."""
+    (delta[q, j, :]), the row's exact L2 sums before their rounding to the
+    per-slot output type (ox[q, j, :]) and the contraction-error bound of each
+    (oeps[q, j, :], zero for the BF16 recipe); masked slots keep NaN rows.
+    Returns (y_rows, hq, delta, ox, oeps, status)."""
     T, H, I, E, k, recipe = p["T"], p["H"], p["I"], p["E"], p["k"], p["recipe"]
     x, x_sf, idx, w, w1, w1_sf, w2, w2_sf = _args(p)
     toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int64))
     y = np.zeros((len(toks), H), np.float32 if y_fp32 else np.uint16)
     hq = np.full((len(toks), k, I), np.nan, np.float64)
     delta = np.full((len(toks), k, I), np.nan, np.float64)
+    ox = np.full((len(toks), k, H), np.nan, np.float64)
+    oeps = np.full((len(toks), k, H), np.nan, np.float64)
     prob = _problem(T, H, I, E, k, recipe, y_fp32, clamp)
     rc = lib().oracle_forward_tokens_rows(ctypes.byref(prob), _ptr(x), _ptr(x_sf), _ptr(idx), _ptr(w),
                                           _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
-                                          _ptr(toks), len(toks), _ptr(y), float(rho), _ptr(hq), _ptr(delta))
+                                          _ptr(toks), len(toks), _ptr(y), float(rho), _ptr(hq), _ptr(delta),
+                                          _ptr(ox), _ptr(oeps))
     if rc < 0:
         raise RuntimeError(f"oracle_forward_tokens_rows failed: {rc}")
-    return y, hq, delta, rc
+    return y, hq, delta, ox, oeps, rc
 
 
 def ffn_row(p: dict, t: int, e: int, clamp: float, rho: float = 0.0):
-    """Intermediates of one routed row: L1 output, activation, re-quantised h, h codes/scales, L2 output,
-    and the rounding-decision band of each re-quantised element for `rho`."""
+    """Intermediates of one routed row: L1 output, activation, re-quantised h, h codes/scales, L2 output
+    (fp32 for the BF16 recipe, bf16 values for the e4m3 recipes), its exact sums before that rounding
+    and their contraction-error bound for `rho`, and the rounding-decision band of each re-quantised
+    element for `rho`."""
     T, H, I, E, k, recipe = p["T"], p["H"], p["I"], p["E"], p["k"], p["recipe"]
     x, x_sf, idx, w, w1, w1_sf, w2, w2_sf = _args(p)
     c = np.zeros(2 * I, np.float32)
@@ -227,16 +235,19 @@ def ffn_row(p: dict, t: int, e: int, clamp: float, rho: float = 0.0):
     hsf = np.zeros(I // 32, np.uint8)
     o = np.zeros(H, np.float32)
     delta = np.zeros(I, np.float64)
+    ox = np.zeros(H, np.float64)
+    oeps = np.zeros(H, np.float64)
     prob = _problem(T, H, I, E, k, recipe, 1, clamp)
     rc = lib().oracle_ffn_row(ctypes.byref(prob), _ptr(x), _ptr(x_sf), int(t), int(e),
                               _ptr(w1), _ptr(w1_sf), _ptr(w2), _ptr(w2_sf),
                               _ptr(c), _ptr(h), _ptr(hq), _ptr(codes), _ptr(hsf), _ptr(o),
-                              float(rho), _ptr(delta))
+                              float(rho), _ptr(delta), _ptr(ox), _ptr(oeps))
     if rc < 0:
         raise RuntimeError(f"oracle_ffn_row failed: {rc}")
     if recipe == RECIPE_FP8_B128:   # one fp32 scale per 1 x 128 block
         hsf = hsf.view(np.float32)
-    return {"c": c, "h": h, "hq": hq, "h_codes": codes, "h_sf": hsf, "o": o, "delta": delta}
+    return {"c": c, "h": h, "hq": hq, "h_codes": codes, "h_sf": hsf, "o": o, "delta": delta, "o_exact": ox,
+            "o_eps": oeps}
 
 
 def quantize_act(x_bits: np.ndarray):

@@ -372,7 +372,7 @@ static void requant_band(const float* h, const float* c, const double* eps, int6
 static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, int64_t t, int64_t e,
                    const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
                    float* c_out, float* h_out, double* hq_out, void* hq_codes, uint8_t* hq_sf, float* o_out,
-                   double rho, double* o_allow, double* delta_out) {
+                   double rho, double* o_allow, double* delta_out, double* o_exact, double* o_eps) {
     const int64_t H = p->hidden, I = p->intermediate;
     double* xd = (double*)malloc(sizeof(double) * (size_t)H);
     double* wd = (double*)malloc(sizeof(double) * (size_t)(H > I ? H : I));
@@ -445,7 +445,14 @@ static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
         }
     }
     /* O6: L2 = hq . W2[e]^T over the intermediate dimension, exact in double,
-       rounded once to fp32 (the per-slot result stays fp32 until the combine). */
+       rounded once to the per-slot output type: fp32 for the BF16 recipe, bf16
+       (round to nearest even) for the e4m3 recipes, whose y is bf16 (a
+       reading: the pages name y's type, not that of the per-expert results the
+       combine adds).  o_exact receives the exact sums; o_eps (e4m3 recipes)
+       the bound of the blocked contraction's error on each, the model of
+       requant_band applied to hq and W2: rho * (sum over 128-element steps of
+       the step's largest |hq_i w_ni|) + steps * 2^-24 * sum_i |hq_i w_ni|
+       (twice that for the (1, 128, 128) recipe). */
     {
         double* delta = NULL;
         if (want_band) {
@@ -460,7 +467,24 @@ static int ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, 
         }
         for (n = 0; n < H; n++) {
             dequant_weight_row(p->recipe, w2, w2_sf, e * H + n, I, wd);
-            o_out[n] = (float)dot(hq, wd, I);
+            {
+                double v = dot(hq, wd, I);
+                o_out[n] = p->recipe == OR_RECIPE_BF16 ? (float)v : (float)oracle_round_bf16(v);
+                if (o_exact) o_exact[n] = v;
+            }
+            if (o_eps) {
+                double S = 0.0, A = 0.0, m = 0.0;
+                int64_t steps = (I + 127) / 128;
+                for (i = 0; i < I; i++) {
+                    double a = fabs(hq[i] * wd[i]);
+                    A += a;
+                    if (a > m) m = a;
+                    if (i % 128 == 127 || i == I - 1) { S += m; m = 0.0; }
+                }
+                o_eps[n] = p->recipe == OR_RECIPE_BF16
+                               ? 0.0
+                               : rho * S + (double)steps * (p->recipe == OR_RECIPE_FP8_B128 ? 2.0 : 1.0) * ldexp(A, -24);
+            }
             if (o_allow) {
                 double a = 0.0;
                 if (delta)
@@ -553,7 +577,8 @@ static int check_problem(const oracle_problem* p) {
 /*
  * Full routed forward.  y rows [0, T) are written; optional outputs:
  *   counts[E], offsets[E+1], row_to_slot[T*k] (first R entries used),
- *   slot_to_row[T*k], o_rows[T*k, H] fp32 per routed row.
+ *   slot_to_row[T*k], o_rows[T*k, H]: each routed row's L2 result (O6) as fp32
+ *   (bf16 values for the e4m3 recipes).
  * Returns OR_OK, OR_BAD_EXPERT_INDEX (y still computed with those slots
  * masked) or a negative error.
  */
@@ -585,7 +610,7 @@ int oracle_forward(const oracle_problem* p, const void* x, const uint8_t* x_sf,
         int64_t e = 0;
         while (offsets[e + 1] <= r) e++;
         if (ffn_row(p, x, x_sf, r2s[r] / k, e, w1, w1_sf, w2, w2_sf, NULL, NULL, NULL, NULL, NULL, o + r * H,
-                    0.0, NULL, NULL) != OR_OK)
+                    0.0, NULL, NULL, NULL, NULL) != OR_OK)
             err |= 1;
     }
     if (err) { free(counts); free(offsets); free(r2s); free(s2r); free(o); return OR_NO_MEMORY; }
@@ -617,13 +642,16 @@ int oracle_forward(const oracle_problem* p, const void* x, const uint8_t* x_sf,
  * routed forward cannot reach in seconds, and as an independent path to the
  * routed one.  When allow_rows is not NULL it receives, per output element,
  * sum_j |w_j| * sum_i delta_i |W2(e_j, n, i)|: the largest change of y that
- * re-quantisation decisions inside the band `rho` can cause (requant_band).
+ * re-quantisation decisions inside the band `rho` can cause (requant_band),
+ * before the rounding of each slot's L2 result to its type (O6; that
+ * rounding's own decisions are bounded from ox_rows / oeps_rows).
  */
 static int forward_tokens_impl(const oracle_problem* p, const void* x, const uint8_t* x_sf,
                                const int32_t* topk_idx, const float* topk_w,
                                const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
                                const int64_t* tokens, int64_t ntok, void* y_rows,
-                               double rho, double* allow_rows, double* hq_rows, double* delta_rows) {
+                               double rho, double* allow_rows, double* hq_rows, double* delta_rows,
+                               double* ox_rows, double* oeps_rows) {
     int64_t H, I, E, k, q;
     int err = 0, bad = 0;
     if (check_problem(p) != OR_OK) return OR_BAD_ARG;
@@ -642,7 +670,9 @@ static int forward_tokens_impl(const oracle_problem* p, const void* x, const uin
             if (e >= 0 && e < E) {
                 if (ffn_row(p, x, x_sf, t, e, w1, w1_sf, w2, w2_sf, NULL, NULL,
                             hq_rows ? hq_rows + (q * k + j) * I : NULL, NULL, NULL, o + j * H,
-                            rho, oa ? oa + j * H : NULL, delta_rows ? delta_rows + (q * k + j) * I : NULL) != OR_OK)
+                            rho, oa ? oa + j * H : NULL, delta_rows ? delta_rows + (q * k + j) * I : NULL,
+                            ox_rows ? ox_rows + (q * k + j) * H : NULL,
+                            oeps_rows ? oeps_rows + (q * k + j) * H : NULL) != OR_OK)
                     err |= 1;
             } else if (e != -1) {
                 bad |= 1;
@@ -673,21 +703,25 @@ int oracle_forward_tokens_band(const oracle_problem* p, const void* x, const uin
                                const int64_t* tokens, int64_t ntok, void* y_rows,
                                double rho, double* allow_rows) {
     return forward_tokens_impl(p, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, tokens, ntok, y_rows, rho,
-                               allow_rows, NULL, NULL);
+                               allow_rows, NULL, NULL, NULL, NULL);
 }
 
 /* Per-token forward that also hands back, for slot j of listed token q (row
    q*k + j of hq_rows / delta_rows, each [ntok*k, I]), the re-quantised
    activation values of that routed row and the rounding-decision band of each
-   of them for `rho` (requant_band; zero for the BF16 recipe).  Rows of masked
-   slots are left untouched.  For unit checks of an implementation's h. */
+   of them for `rho` (requant_band; zero for the BF16 recipe), and (rows
+   q*k + j of ox_rows / oeps_rows, each [ntok*k, H]; either may be NULL) the
+   exact L2 sums of the row before their rounding to the per-slot type and the
+   contraction-error bound of each (O6).  Rows of masked slots are left
+   untouched.  For unit checks of an implementation's h and o. */
 int oracle_forward_tokens_rows(const oracle_problem* p, const void* x, const uint8_t* x_sf,
                                const int32_t* topk_idx, const float* topk_w,
                                const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
                                const int64_t* tokens, int64_t ntok, void* y_rows,
-                               double rho, double* hq_rows, double* delta_rows) {
+                               double rho, double* hq_rows, double* delta_rows, double* ox_rows,
+                               double* oeps_rows) {
     return forward_tokens_impl(p, x, x_sf, topk_idx, topk_w, w1, w1_sf, w2, w2_sf, tokens, ntok, y_rows, rho,
-                               NULL, hq_rows, delta_rows);
+                               NULL, hq_rows, delta_rows, ox_rows, oeps_rows);
 }
 
 int oracle_forward_tokens(const oracle_problem* p, const void* x, const uint8_t* x_sf,
@@ -704,11 +738,11 @@ int oracle_forward_tokens(const oracle_problem* p, const void* x, const uint8_t*
 int oracle_ffn_row(const oracle_problem* p, const void* x, const uint8_t* x_sf, int64_t t, int64_t e,
                    const void* w1, const uint8_t* w1_sf, const void* w2, const uint8_t* w2_sf,
                    float* c_out, float* h_out, double* hq_out, void* hq_codes, uint8_t* hq_sf, float* o_out,
-                   double rho, double* delta_out) {
+                   double rho, double* delta_out, double* o_exact, double* o_eps) {
     if (check_problem(p) != OR_OK) return OR_BAD_ARG;
     if (t < 0 || t >= p->num_tokens || e < 0 || e >= p->num_experts || !o_out) return OR_BAD_ARG;
     return ffn_row(p, x, x_sf, t, e, w1, w1_sf, w2, w2_sf, c_out, h_out, hq_out, hq_codes, hq_sf, o_out,
-                   rho, NULL, delta_out);
+                   rho, NULL, delta_out, o_exact, o_eps);
 }
 
 /* ------------------------------------------------------------------------ */

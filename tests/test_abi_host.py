@@ -53,11 +53,12 @@ def test_workspace_size_depends_on_problem_only_and_grows_with_tokens():
              for t in (0, 1, 128, 8192)]
     assert sizes == sorted(sizes) and sizes[0] > 0
     v = mf.get_workspace_view(mf.make_problem(128, 7168, 2048, 256, 8, mf.RECIPE_FP8_FP4))
-    assert v.h_row_bytes == 2048 and v.h_sf_row_bytes == 64 and v.o_row_bytes == 7168 * 4
+    # per routed row: e4m3 h codes, one e8m0 byte per 32, and the L2 result in bf16
+    assert v.h_row_bytes == 2048 and v.h_sf_row_bytes == 64 and v.o_row_bytes == 7168 * 2
     assert v.h % 256 == 0 and v.h_sf % 256 == 0 and v.o % 256 == 0
-    assert v.o + 128 * 8 * 7168 * 4 <= sizes[2]
+    assert v.o + 128 * 8 * 7168 * 2 <= sizes[2]
     vb = mf.get_workspace_view(mf.make_problem(64, 256, 128, 8, 2, mf.RECIPE_BF16))
-    assert vb.h_row_bytes == 256 and vb.h_sf_row_bytes == 0
+    assert vb.h_row_bytes == 256 and vb.h_sf_row_bytes == 0 and vb.o_row_bytes == 256 * 4   # fp32 L2 result
 
 
 def test_token_alignment_and_strerror():

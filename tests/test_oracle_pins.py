@@ -226,6 +226,35 @@ def _torch_dequant_w(p, which, e, n):
     return [Fraction(float(vals[kk])) * Fraction(float(sc[kk // 32])) for kk in range(len(vals))]
 
 
+def _bf16_rne_exact(x: Fraction) -> Fraction:
+    """Round a rational to bf16 (8 significant bits, round half to even) in exact arithmetic: the
+    spacing at |x| in [2^e, 2^(e+1)) is 2^(e-7) (normal range only; the values here are far from it)."""
+    if x == 0:
+        return Fraction(0)
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    sp = Fraction(2) ** (e - 7)
+    q = a / sp
+    f = q.numerator // q.denominator
+    r = q - f
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    return (f * sp) if x > 0 else -(f * sp)
+
+
+def test_bf16_rne_exact_helper_on_hand_values():
+    # 1 + 2^-8 is the midpoint between 1 and 1 + 2^-7: ties go to the even code (1); a hair above goes up
+    assert _bf16_rne_exact(Fraction(1) + Fraction(1, 256)) == 1
+    assert _bf16_rne_exact(Fraction(1) + Fraction(3, 256)) == Fraction(1) + Fraction(2, 128)
+    assert _bf16_rne_exact(Fraction(1) + Fraction(1, 256) + Fraction(1, 2 ** 40)) == Fraction(1) + Fraction(1, 128)
+    assert _bf16_rne_exact(Fraction(-6266285645, 10 ** 6)) == -6272          # spacing 32 in [4096, 8192)
+    # 255 has 8 significant bits (exact); in [256, 512) the spacing is 2: 257 ties to 256, 259 to 260
+    assert _bf16_rne_exact(Fraction(-255)) == -255
+    assert _bf16_rne_exact(Fraction(257)) == 256 and _bf16_rne_exact(Fraction(259)) == 260
+
+
 @pytest.mark.parametrize("recipe", [synth.RECIPE_BF16, synth.RECIPE_FP8_FP8, synth.RECIPE_FP8_FP4,
                                     synth.RECIPE_FP8_B128])
 def test_gemms_exact_rationals(recipe):
@@ -243,7 +272,13 @@ def test_gemms_exact_rationals(recipe):
     for n in range(p["H"]):
         wq = _torch_dequant_w(p, "w2", e, n)
         exact = sum(a * b for a, b in zip(hq, wq))
-        assert np.float32(float(exact)) == row["o"][n], n
+        if recipe == synth.RECIPE_BF16:
+            assert np.float32(float(exact)) == row["o"][n], n   # fp32 per-slot result
+        else:                                                    # bf16 per-slot result: one rounding
+            assert Fraction(float(row["o"][n])) == _bf16_rne_exact(exact), n
+        # the exact sum before that rounding, to double accuracy
+        mag = sum(abs(a * b) for a, b in zip(hq, wq))
+        assert abs(Fraction(float(row["o_exact"][n])) - exact) <= mag * Fraction(len(hq) + 1, 2 ** 53), n
 
 
 def test_requant_row_codes_decode_to_hq_and_obey_scale_rule():
@@ -312,7 +347,8 @@ def _identical_experts(p):
 
 
 def _dense_ffn_torch(p, t, clamp):
-    """One dense SwiGLU FFN (expert 0) on token t with torch float64 linear algebra and torch casts."""
+    """One dense SwiGLU FFN (expert 0) on token t with torch float64 linear algebra and torch casts; the
+    result rounded once to the per-slot output type (fp32, or bf16 for the e4m3 recipes)."""
     x = torch.tensor([float(v) for v in _torch_dequant_act(p, t)], dtype=torch.float64)
     W1 = torch.tensor([[float(v) for v in _torch_dequant_w(p, "w1", 0, n)] for n in range(2 * p["I"])],
                       dtype=torch.float64)
@@ -343,7 +379,11 @@ def _dense_ffn_torch(p, t, clamp):
                 while 448.0 * 2.0 ** E < amax:
                     E += 1
             hq[32 * b:32 * b + 32] = (blk * 2.0 ** -E).float().to(torch.float8_e4m3fn).double() * 2.0 ** E
-    return torch.nn.functional.linear(hq, W2).float()
+    o = torch.nn.functional.linear(hq, W2)
+    if p["recipe"] == synth.RECIPE_BF16:
+        return o.float()
+    # e4m3 recipes: the per-slot result is bf16 (one round-to-nearest-even of the double sum)
+    return torch.tensor([float(_bf16_rne_exact(Fraction(float(v)))) for v in o], dtype=torch.float32)
 
 
 @pytest.mark.parametrize("recipe,k,w", [(synth.RECIPE_FP8_FP4, 2, (0.25, 0.75)),
@@ -486,7 +526,7 @@ def test_forward_tokens_rows_hands_back_each_slots_row():
     p = _small(synth.RECIPE_FP8_FP4, T=8)
     p["topk_idx"][3, 1] = -1
     toks = [6, 1, 3]
-    y, hq, delta, rc = oracle.forward_tokens_rows(p, toks, True, 7.0, 2.0 ** -8)
+    y, hq, delta, ox, oeps, rc = oracle.forward_tokens_rows(p, toks, True, 7.0, 2.0 ** -8)
     assert rc == oracle.OK
     assert np.array_equal(y, oracle.forward_tokens(p, toks, True, 7.0)[0])
     for q, t in enumerate(toks):
@@ -494,10 +534,52 @@ def test_forward_tokens_rows_hands_back_each_slots_row():
             e = int(p["topk_idx"][t, j])
             if e < 0:
                 assert np.all(np.isnan(hq[q, j])) and np.all(np.isnan(delta[q, j]))
+                assert np.all(np.isnan(ox[q, j])) and np.all(np.isnan(oeps[q, j]))
                 continue
             row = oracle.ffn_row(p, t, e, 7.0, rho=2.0 ** -8)
             assert np.array_equal(hq[q, j], row["hq"]) and np.array_equal(delta[q, j], row["delta"])
-    assert np.nanmax(delta) > 0.0
+            assert np.array_equal(ox[q, j], row["o_exact"]) and np.array_equal(oeps[q, j], row["o_eps"])
+            # the per-slot result is the bf16 rounding of the exact sum: within half a bf16 spacing
+            assert np.all(np.abs(row["o"] - ox[q, j]) <= np.abs(ox[q, j]) * 2.0 ** -8)
+    assert np.nanmax(delta) > 0.0 and np.nanmin(oeps) > 0.0
+
+
+def test_parity_bf16_rounding_helpers():
+    # the parity tests' vectorised bf16 rounding (tests/gpu_common.py) against the oracle's pinned
+    # round_bf16, on midpoints between bf16 neighbours (ties), their double neighbours and random values
+    from gpu_common import o_rounding_bound, round_bf16
+    rng = np.random.default_rng(5)
+    base = np.concatenate([np.exp2(rng.uniform(-40, 40, 3000)), rng.uniform(0.5, 1.0, 1000)])
+    grid = np.array([oracle.round_bf16(float(v)) for v in base])
+    step = np.array([abs(oracle.round_bf16(float(g) * (1 + 2.0 ** -7)) - g) for g in grid])   # next grid point up
+    mid = grid + step / 2
+    vals = np.concatenate([base, mid, np.nextafter(mid, 0), np.nextafter(mid, np.inf), grid, [0.0, 2.0 ** -130]])
+    vals = np.concatenate([vals, -vals])
+    ref = np.array([oracle.round_bf16(float(v)) for v in vals])
+    assert np.array_equal(round_bf16(vals), ref)
+    # the rounding bound: no g in [ox - dev, ox + dev] rounds further from bf16(ox) (brute force on a grid)
+    ox = rng.normal(0, 3, 200)
+    dev = np.abs(ox) * np.exp2(rng.uniform(-14, -5, 200))
+    b = o_rounding_bound(ox, dev)
+    for f in np.linspace(-1, 1, 41):
+        assert np.all(np.abs(round_bf16(ox + f * dev) - round_bf16(ox)) <= b)
+    assert np.any(b > 0) and np.any(b == 0)
+
+
+def test_l2_error_bound_closed_form():
+    gold = json.load(open(os.path.join(GOLDEN, "closed_form_example.json")))["o_band"]["expected"]
+    p = _closed_form_problem()
+    _, _, _, ox, oeps, rc = oracle.forward_tokens_rows(p, [0, 1], True, 7.0, gold["rho"])
+    assert rc == oracle.OK
+    # token 0: slot 0 expert 1, slot 1 masked; token 1: slot 0 expert 0, slot 1 expert 1
+    assert np.all(np.isnan(ox[0, 1])) and np.all(np.isnan(oeps[0, 1]))
+    for (q, j), ex in (((0, 0), "expert1"), ((1, 0), "expert0"), ((1, 1), "expert1")):
+        assert np.all(ox[q, j] == gold["exact"][ex]), (q, j)
+        # 32 equal terms: equal to the hand value up to the rounding of the sums
+        assert np.allclose(oeps[q, j], gold["eps_o"][ex], rtol=1e-12, atol=0.0), (q, j, oeps[q, j][:2])
+    q = _small(synth.RECIPE_BF16, T=4)
+    _, _, _, _, oeps_bf16, _ = oracle.forward_tokens_rows(q, [0, 1], True, 7.0, 0.1)
+    assert np.all((oeps_bf16 == 0.0) | np.isnan(oeps_bf16))
 
 
 # --------------------------------------------------------------------------
