@@ -1649,17 +1649,26 @@ __device__ __forceinline__ void phase_big_tiles(const KParams& p, Shared& sh, co
   // Thread 0 keeps one claim in flight while a tile runs: a fetch-and-add on
   // the counter of range `cur` (first the XCD's own), issued before the tile
   // and resolved after it, so its round trip to the memory-side atomics
-  // overlaps the tile instead of standing between two tiles.
+  // overlaps the tile instead of standing between two tiles.  Within the last
+  // `near` tiles of a range the next claim waits for the tile's end: a tile
+  // claimed ahead there could start only after the list has drained and
+  // would stretch the phase's tail by a whole tile.
+  const uint32_t near = gridDim.x >> 2;  // ~2 tiles per workgroup of an XCD
   int cur = xcc_id();
   uint32_t pend = 0;
-  if (tid == 0) pend = __hip_atomic_fetch_add(&ctr[cur], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bool held = false;
   for (;;) {
-    if (tid == 0) sh.tile = resolve_big_claim(ctr, n, cur, pend);
+    if (tid == 0) {
+      if (!held) pend = __hip_atomic_fetch_add(&ctr[cur], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t tc = resolve_big_claim(ctr, n, cur, pend);
+      sh.tile = tc;
+      held = tc < n && tc + near < big_range_begin(n, cur + 1);
+      if (held) pend = __hip_atomic_fetch_add(&ctr[cur], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     __syncthreads();
     const uint32_t t = __builtin_amdgcn_readfirstlane(sh.tile);
     __syncthreads();
     if (t >= n) break;
-    if (tid == 0) pend = __hip_atomic_fetch_add(&ctr[cur], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     int e, mb, nb;
     decode_big_tile(sh, E, NB, (int)t, e, mb, nb);
     e = __builtin_amdgcn_readfirstlane(e);
@@ -1716,9 +1725,12 @@ __device__ __forceinline__ void combine_store8(const KParams& p, int t, int c, c
   }
 }
 
-// bf16 rows of o (e4m3 recipes).  H is a multiple of 32, so no 8-column
-// piece straddles the end of a row.
-__device__ void phase_combine_b16(const KParams& p, int myrow, float myw) {
+// bf16 rows of o (e4m3 recipes).  A wave takes U units at a time (its units
+// u, u + nw, .., u + (U-1) nw), all their loads in flight together, and
+// fetches the slots of its next U units while they stream in.  H is a
+// multiple of 32, so no 8-column piece straddles the end of a row.
+template <int U>
+__device__ void phase_combine_b16(const KParams& p, int row0, float w0) {
   const int lane = threadIdx.x & 63;
   const int H = p.H, k = p.k;
   const int nw = gridDim.x * 4;
@@ -1726,54 +1738,101 @@ __device__ void phase_combine_b16(const KParams& p, int myrow, float myw) {
   const int units = p.T * nc;
   const int u0 = blockIdx.x * 4 + (threadIdx.x >> 6);
   const uint16_t* o = (const uint16_t*)p.o;
-  for (int u = u0; u < units; u += nw) {
-    const int t = u / nc, cu = u - t * nc;
-    if (u != u0) {  // lane j < k holds slot j's row and weight
-      myrow = lane < k ? p.s2r[(size_t)t * k + lane] : -1;
-      myw = lane < k ? p.tw[(size_t)t * k + lane] : 0.f;
+  // lane j < k: slot j's row and weight, for each of the wave's next U units
+  // (a unit past the end repeats the last one: loads stay in bounds, nothing is stored)
+  int mrow[U];
+  float mw[U];
+  mrow[0] = row0;
+  mw[0] = w0;
+#pragma unroll
+  for (int q = 1; q < U; q++) {
+    const int tq = min(u0 + q * nw, units - 1) / nc;
+    mrow[q] = lane < k ? p.s2r[(size_t)tq * k + lane] : -1;
+    mw[q] = lane < k ? p.tw[(size_t)tq * k + lane] : 0.f;
+  }
+  for (int u = u0; u < units; u += U * nw) {
+    int crow[U], tt[U], ca[U], la[U], lb[U];
+    float cw[U];
+    bool live[U], va[U], vb[U];
+#pragma unroll
+    for (int q = 0; q < U; q++) {
+      const int uq = u + q * nw;
+      live[q] = uq < units;
+      const int uc = live[q] ? uq : u;
+      tt[q] = uc / nc;
+      const int cu = uc - tt[q] * nc;
+      const int cend = min(H, (cu + 1) << 10);
+      ca[q] = (cu << 10) + lane * 8;
+      va[q] = ca[q] < cend;
+      vb[q] = ca[q] + 512 < cend;
+      // lanes past the row's end read column 0 and drop it: every load is
+      // issued unconditionally, so all of them are in flight together
+      la[q] = va[q] ? ca[q] : 0;
+      lb[q] = vb[q] ? ca[q] + 512 : 0;
+      crow[q] = mrow[q];
+      cw[q] = mw[q];
     }
-    const int cend = min(H, (cu + 1) << 10);
-    const int ca = (cu << 10) + lane * 8, cb = ca + 512;
-    const bool va = ca < cend, vb = cb < cend;
-    float acc[16];
+    float acc[U][16];
 #pragma unroll
-    for (int i = 0; i < 16; i++) acc[i] = 0.f;
+    for (int q = 0; q < U; q++)
+#pragma unroll
+      for (int i = 0; i < 16; i++) acc[q][i] = 0.f;
     for (int j0 = 0; j0 < k; j0 += 8) {
-      v4i oa[8], ob[8];
-      int rows[8];
-      float ws[8];
+      v4i oa[U][8], ob[U][8];
+      int rows[U][8];
+      float ws[U][8];
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int jj = j0 + j;
-        rows[j] = jj < k ? __shfl(myrow, jj, 64) : -1;
-        ws[j] = jj < k ? __shfl(myw, jj, 64) : 0.f;
-        const size_t base = (size_t)(rows[j] < 0 ? 0 : rows[j]) * H;
-        oa[j] = (rows[j] >= 0 && va) ? ldg16(o + base + ca) : v4i{0, 0, 0, 0};
-        ob[j] = (rows[j] >= 0 && vb) ? ldg16(o + base + cb) : v4i{0, 0, 0, 0};
+      for (int q = 0; q < U; q++) {
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+          const int jj = j0 + j;
+          // slot jj's row and weight, wave-uniform (a masked slot, or one past k, has row -1 and reads row 0)
+          rows[q][j] = jj < k ? __builtin_amdgcn_readlane(crow[q], jj) : -1;
+          ws[q][j] = jj < k ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cw[q]), jj)) : 0.f;
+          const size_t base = (size_t)(rows[q][j] < 0 ? 0 : rows[q][j]) * H;
+          oa[q][j] = ldg16(o + base + la[q]);
+          ob[q][j] = ldg16(o + base + lb[q]);
+        }
+      }
+      if (j0 == 0) {
+#pragma unroll
+        for (int q = 0; q < U; q++) {
+          const int tn = min(u + (U + q) * nw, units - 1) / nc;
+          mrow[q] = lane < k ? p.s2r[(size_t)tn * k + lane] : -1;
+          mw[q] = lane < k ? p.tw[(size_t)tn * k + lane] : 0.f;
+        }
       }
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        if (rows[j] >= 0) {
+      for (int q = 0; q < U; q++) {
 #pragma unroll
-          for (int c = 0; c < 4; c++) {
-            const uint32_t a = (uint32_t)oa[j][c], b = (uint32_t)ob[j][c];
-            acc[2 * c] = __builtin_fmaf(ws[j], __uint_as_float(a << 16), acc[2 * c]);
-            acc[2 * c + 1] = __builtin_fmaf(ws[j], __uint_as_float(a & 0xFFFF0000u), acc[2 * c + 1]);
-            acc[8 + 2 * c] = __builtin_fmaf(ws[j], __uint_as_float(b << 16), acc[8 + 2 * c]);
-            acc[8 + 2 * c + 1] = __builtin_fmaf(ws[j], __uint_as_float(b & 0xFFFF0000u), acc[8 + 2 * c + 1]);
+        for (int j = 0; j < 8; j++) {
+          if (rows[q][j] >= 0) {
+#pragma unroll
+            for (int c = 0; c < 4; c++) {
+              const uint32_t a = (uint32_t)oa[q][j][c], b = (uint32_t)ob[q][j][c];
+              acc[q][2 * c] = __builtin_fmaf(ws[q][j], __uint_as_float(a << 16), acc[q][2 * c]);
+              acc[q][2 * c + 1] = __builtin_fmaf(ws[q][j], __uint_as_float(a & 0xFFFF0000u), acc[q][2 * c + 1]);
+              acc[q][8 + 2 * c] = __builtin_fmaf(ws[q][j], __uint_as_float(b << 16), acc[q][8 + 2 * c]);
+              acc[q][8 + 2 * c + 1] = __builtin_fmaf(ws[q][j], __uint_as_float(b & 0xFFFF0000u), acc[q][8 + 2 * c + 1]);
+            }
           }
         }
       }
     }
-    if (va) combine_store8(p, t, ca, acc);
-    if (vb) combine_store8(p, t, cb, acc + 8);
+#pragma unroll
+    for (int q = 0; q < U; q++) {
+      if (live[q]) {
+        if (va[q]) combine_store8(p, tt[q], ca[q], acc[q]);
+        if (vb[q]) combine_store8(p, tt[q], ca[q] + 512, acc[q] + 8);
+      }
+    }
   }
 }
 
 template <int RECIPE, bool WIDE>
 __device__ void phase_combine(const KParams& p, int myrow, float myw) {
   if constexpr (RECIPE != 0) {
-    phase_combine_b16(p, myrow, myw);
+    phase_combine_b16<2>(p, myrow, myw);
     return;
   }
   const float* o = (const float*)p.o;

@@ -1,0 +1,38 @@
+// Test helper: the forward's hardware pack conversions (e4m3x4 and bf16x2 of
+// the device helpers) applied to a list of floats, so that a test can compare
+// them with the oracle's encoders value by value.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../mixture_experts_ffn_histogram_amd/csrc/moe_ffn_device.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void convert(const float* __restrict__ in, uint32_t* __restrict__ out, int nquads) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < nquads) out[i] = moeffn::e4m3x4(in[4 * i], in[4 * i + 1], in[4 * i + 2], in[4 * i + 3]);
+}
+
+__global__ __launch_bounds__(256) void convert_bf16(const float* __restrict__ in, uint32_t* __restrict__ out, int npairs) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < npairs) out[i] = moeffn::bf16x2(in[2 * i], in[2 * i + 1]);
+}
+
+}  // namespace
+
+// in: 4 * nquads floats (device), out: nquads dwords (device), byte j of out[i] = code of in[4 i + j].
+extern "C" int moe_test_e4m3x4(const float* in, uint32_t* out, int nquads, void* stream) {
+  if (nquads <= 0) return 0;
+  hipLaunchKernelGGL(convert, dim3((nquads + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), in, out,
+                     nquads);
+  return (int)hipGetLastError();
+}
+
+// in: 2 * npairs floats (device), out: npairs dwords (device), low half of out[i] = bf16 bits of in[2 i],
+// high half those of in[2 i + 1].
+extern "C" int moe_test_bf16x2(const float* in, uint32_t* out, int npairs, void* stream) {
+  if (npairs <= 0) return 0;
+  hipLaunchKernelGGL(convert_bf16, dim3((npairs + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), in,
+                     out, npairs);
+  return (int)hipGetLastError();
+}

@@ -1,4 +1,4 @@
-"""The forward's packed e4m3 conversion against the oracle's encoder (MI355X only).
+"""The forward's hardware pack conversions against the oracle's encoders (MI355X only).
 
 The L1 epilogues and the pre-dispatch quantiser write their e4m3 codes with
 the hardware pack conversion (`e4m3x4` in the device helpers).  Its codes
@@ -7,7 +7,13 @@ encoder) for every
 value the kernels can hand it: every e4m3 value, every midpoint between
 neighbouring values and the floats next to it, fp32 denormals, magnitudes in
 (448, 464] (the fp32-scale recipe's quotient can pass 448 by an ulp), and
-random values over the whole range, uniform and log-uniform."""
+random values over the whole range, uniform and log-uniform.
+
+The L2 epilogues round each slot's result to bf16 with the other pack
+conversion (`bf16x2`): its bits must be the oracle's round-to-nearest-even
+bf16 for every bf16 value, every midpoint between neighbours and the floats
+next to it, fp32 denormals and random finite values below 2^127 (the
+results are far from overflow; NaN is not an input)."""
 import ctypes
 import os
 
@@ -40,7 +46,7 @@ def conversion_inputs() -> np.ndarray:
 
 
 def test_e4m3x4_matches_oracle_encoder():
-    path = os.path.join(HERE, "native", "libmoe_e4m3.so")
+    path = os.path.join(HERE, "native", "libmoe_convert.so")
     if not os.path.exists(path):
         pytest.fail(f"{path} is missing: build it with mixture_experts_ffn_histogram_amd/build.py build_test_helpers()")
     lib = ctypes.CDLL(path)
@@ -58,3 +64,40 @@ def test_e4m3x4_matches_oracle_encoder():
     bad = np.nonzero(got != ref)[0]
     assert bad.size == 0, (f"{bad.size} of {v.size} codes differ, first: "
                            + ", ".join(f"{v[i]!r}: gpu 0x{got[i]:02x} oracle 0x{ref[i]:02x}" for i in bad[:6]))
+
+
+def bf16_inputs() -> np.ndarray:
+    bits = np.arange(0x0000, 0x7F80, dtype=np.uint32)                       # every finite non-negative bf16
+    vals = (bits << 16).view(np.float32)
+    vals = vals[vals < np.float32(2.0 ** 127)]
+    nxt = ((bits + 1) << 16).view(np.float32)[: vals.size]
+    mid = vals + (nxt - vals) / np.float32(2)                                # exact: 9 significant bits
+    mid = mid[np.isfinite(mid)]
+    near = np.concatenate([np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(np.inf))])
+    den = np.arange(1, 4097, dtype=np.uint32).view(np.float32)               # fp32 denormals
+    rng = np.random.default_rng(77)
+    rnd = rng.integers(0, 0x7F000000, 200_000, dtype=np.uint32).view(np.float32)
+    v = np.concatenate([vals, mid, near, den, rnd])
+    v = np.concatenate([v, -v]).astype(np.float32)
+    return np.concatenate([v, np.zeros(v.size % 2, np.float32)])
+
+
+def test_bf16x2_matches_oracle_rounding():
+    path = os.path.join(HERE, "native", "libmoe_convert.so")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} is missing: build it with mixture_experts_ffn_histogram_amd/build.py build_test_helpers()")
+    lib = ctypes.CDLL(path)
+    lib.moe_test_bf16x2.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.moe_test_bf16x2.restype = ctypes.c_int
+    v = bf16_inputs()
+    n2 = v.size // 2
+    x = torch.from_numpy(v).cuda()
+    out = torch.zeros(n2, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    assert lib.moe_test_bf16x2(x.data_ptr(), out.data_ptr(), n2, stream.cuda_stream) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)                               # half j of dword i = value 2 i + j
+    ref = np.fromiter((oracle.enc_bf16(oracle.round_bf16(float(a))) for a in v), np.uint16, count=v.size)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (f"{bad.size} of {v.size} values differ, first: "
+                           + ", ".join(f"{v[i]!r}: gpu 0x{got[i]:04x} oracle 0x{ref[i]:04x}" for i in bad[:6]))
