@@ -1252,30 +1252,38 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
       stg4(p.hsg + (size_t)nb * p.sg_rows + (size_t)(row0 + tid), sw);
     }
   } else {
-    // o through LDS, one 16-row block t at a time (the ring buffers are free:
-    // the K loop ends on a barrier): the waves' 16 x 64 values go to buffer
-    // t % 3 as [row][256 outputs] (row stride 1 KB + 16 bytes), then each
-    // wave stores 4 whole rows of the tile's 256 outputs, 1 KB contiguous per
-    // instruction (8 whole cache lines instead of 64-byte pieces of 16 rows).
-    // A buffer is written again three blocks later, after two more barriers
-    // that every wave reaches only once done reading it.  Waves whose rows
-    // lie past H (the last block of an odd H/128) write nothing but store the
-    // other waves' outputs.
-    constexpr int kOStride = 1040;
-    const int c0 = nb * 256 + lane * 4;
+    // o through LDS, two 16-row blocks at a time (the ring buffers are free:
+    // the K loop ends on a barrier): the waves' values of blocks 2q and 2q+1,
+    // rounded to bf16, go to buffer q % 3 as [32 rows][256 outputs] (row
+    // stride 512 + 16 bytes), then every store instruction writes two whole
+    // 512-byte rows of the tile's outputs (lanes 0-31 and 32-63, 16 bytes
+    // each).  A buffer is written again three pairs later, after two more
+    // barriers that every wave reaches only once done reading it.  Waves
+    // whose rows lie past H (the last block of an odd H/128) write nothing
+    // but store the other waves' outputs.
+    constexpr int kOStride = 528;
+    static_assert(32 * kOStride <= kBigBuf, "a pair of 16-row blocks of o fits a ring buffer");
+    const int col = (lane & 31) * 8;  // this lane's 8 outputs of the tile's 256
 #pragma unroll
-    for (int t = 0; t < NT; t++) {
-      uint8_t* bp = t % 3 == 0 ? R.b0 : t % 3 == 1 ? R.b1 : R.b2;
+    for (int tp = 0; tp < NT / 2; tp++) {
+      uint8_t* bp = tp % 3 == 0 ? R.b0 : tp % 3 == 1 ? R.b1 : R.b2;
       if (active) {
 #pragma unroll
-        for (int j = 0; j < 4; j++) *(v4f*)(bp + r16 * kOStride + (wave * 64 + 16 * j + 4 * g) * 4) = acc[j][t];
+        for (int hb = 0; hb < 2; hb++)
+#pragma unroll
+          for (int j = 0; j < 4; j++) {
+            const v4f& a = acc[j][2 * tp + hb];
+            *(uint2*)(bp + (hb * 16 + r16) * kOStride + (wave * 64 + 16 * j + 4 * g) * 2) =
+                uint2{bf16x2(a[0], a[1]), bf16x2(a[2], a[3])};
+          }
       }
       __syncthreads();
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
-        const int m = t * 16 + wave * 4 + rr;
-        const v4f v = *(const v4f*)(bp + (wave * 4 + rr) * kOStride + lane * 16);
-        if (m < nrows && c0 < H) store_o4<RECIPE>(p, (size_t)(row0 + m) * H + (size_t)c0, v);
+        const int lr = wave * 8 + rr * 2 + (lane >> 5);  // row of the pair
+        const int m = tp * 32 + lr;
+        const v4i v = *(const v4i*)(bp + lr * kOStride + col * 2);
+        if (m < nrows && nb * 256 + col < H) stg16((uint16_t*)p.o + (size_t)(row0 + m) * H + (size_t)(nb * 256 + col), v);
       }
     }
   }
