@@ -1048,9 +1048,11 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
   auto compute = [&](int slot, int buf) {
     const uint8_t* bp = BUF(buf);
     int sa[4], sb[NT];
-    // weight scales: the dword of row r16 of block j holds the stage's 4 blocks; lane group g takes byte g
+    // scales: one byte per lane (the dword of row r16 of block j, routed row t*16 + r16, holds the
+    // stage's 4 blocks; lane group g takes byte g), read as bytes: a dword read and a shift per
+    // value measured slower (the shifts sit between the LDS reads and the MFMAs)
 #pragma unroll
-    for (int j = 0; j < 4; j++) sa[j] = (int)(*(const uint32_t*)(bp + sa_base + j * 64) >> (8 * g));
+    for (int j = 0; j < 4; j++) sa[j] = bp[sa_base + j * 64 + g];
 #pragma unroll
     for (int t = 0; t < NT; t++) sb[t] = bp[kBigBsf + (t * 16 + r16) * 4 + g];
     v4i n0 = *(const v4i*)(bp + brd0);
