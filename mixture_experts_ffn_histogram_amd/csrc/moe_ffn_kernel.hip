@@ -1045,31 +1045,35 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
     const uint32_t as_off = (s >> 2) < (nk >> 2) ? as_full : as_last;
     buf_load_lds4(rWs, bp + kBigAsf + wave * 256, live ? as_off : kBufDead, (uint32_t)((s >> 2) * 256 + (s & 3) * 4));
   };
-  auto compute = [&](int slot, int buf) {
+  auto compute = [&](int slot, int buf, auto&& mid) {
     const uint8_t* bp = BUF(buf);
-    int sa[4], sb[NT];
+    int sa[4];
     // scales: one byte per lane (the dword of row r16 of block j, routed row t*16 + r16, holds the
     // stage's 4 blocks; lane group g takes byte g), read as bytes: a dword read and a shift per
     // value measured slower (the shifts sit between the LDS reads and the MFMAs)
 #pragma unroll
     for (int j = 0; j < 4; j++) sa[j] = bp[sa_base + j * 64 + g];
-#pragma unroll
-    for (int t = 0; t < NT; t++) sb[t] = bp[kBigBsf + (t * 16 + r16) * 4 + g];
+    int sbt = bp[kBigBsf + r16 * 4 + g];
     v4i n0 = *(const v4i*)(bp + brd0);
     v4i n1 = *(const v4i*)(bp + brd1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 6 + NT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 7, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mid();  // issued while the first reads are in flight
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < NT; t++) {
       const v8i bb = {n0[0], n0[1], n0[2], n0[3], n1[0], n1[1], n1[2], n1[3]};
-      if (t < NT - 1) {
+      const int sbc = sbt;
+      if (t < NT - 1) {  // the next block's operand and scale, read under this block's MFMAs
+        sbt = bp[kBigBsf + ((t + 1) * 16 + r16) * 4 + g];
         n0 = *(const v4i*)(bp + brd0 + (t + 1) * 2048);
         n1 = *(const v4i*)(bp + brd1 + (t + 1) * 2048);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
       }
 #pragma unroll
       for (int j = 0; j < 4; j++) {
         const v8i aa = {ar[slot][j][0], ar[slot][j][1], ar[slot][j][2], ar[slot][j][3], 0, 0, 0, 0};
-        acc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, acc[j][t], 4, 0, 0, sa[j], 0, sb[t]);
+        acc[j][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aa, bb, acc[j][t], 4, 0, 0, sa[j], 0, sbc);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
@@ -1098,9 +1102,8 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
       const int s = s0 + u;
       MOEFFN_WAIT_VMCNT(big_wait<NT>());  // this wave's fill of stage s has landed
       __builtin_amdgcn_s_barrier();       // ... and every other wave's
-      dma(s + kBigD, (u + kBigD) % kBigNB);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(u, u);
+      // the stage's first LDS reads, then the fill of stage s + D, then the MFMAs
+      compute(u, u, [&] { dma(s + kBigD, (u + kBigD) % kBigNB); });
       load_a(u, s + kBigP);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1111,7 +1114,7 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
     if (s0 + u < nk) {
       MOEFFN_WAIT_VMCNT(0);
       __builtin_amdgcn_s_barrier();
-      compute(u, u);
+      compute(u, u, [] {});
     }
   }
   // every wave is done with the ring before the next tile refills it or the
