@@ -50,7 +50,7 @@ def build_test_helpers(verbose: bool = False) -> list:
     kernel and the e4m3 conversion check."""
     root = os.path.dirname(HERE)
     outs = []
-    for src_name, lib_name in (("side_kernel.hip", "libmoe_side.so"), ("pack_convert.hip", "libmoe_convert.so")):
+    for src_name, lib_name in (("side_kernel.hip", "libmoe_side.so"), ("device_helpers.hip", "libmoe_helpers.so")):
         src = os.path.join(root, "tests", "native", src_name)
         out = os.path.join(root, "tests", "native", lib_name)
         cmd = [HIPCC] + COMMON + ["-shared", "-x", "hip", src, "-o", out + ".tmp"]

@@ -98,6 +98,17 @@ __device__ __forceinline__ uint32_t bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(moe_f32x2{a, b}, moe_bf16x2));
 }
 
+// Largest of a value over lanes l, l^16, l^32 and l^48 (the lanes holding the
+// same index of the four 16-lane rows) with the lane-swap moves of gfx950:
+// the 32-lane swap pairs each lane with lane l^32, the 16-lane swap with l^16.
+// VALU moves, not LDS permutes.
+__device__ __forceinline__ float max_over_rows(float a) {
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  a = __builtin_fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
+  return __builtin_fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
 // Exponent E of the e8m0 scale of a 1x32 block: the smallest integer with
 // amax <= 448 * 2^E (448 = 1.75 * 2^8), clamped to [-127, 127]; 0 for an
 // all-zero block.  Exact on the fp32 bit pattern: with amax = f * 2^p,

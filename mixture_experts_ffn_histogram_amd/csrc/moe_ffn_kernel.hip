@@ -664,8 +664,7 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
 #pragma unroll
           for (int j = 0; j < 4; j++)
             a = __builtin_fmaxf(a, __builtin_fabsf(swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp)));
-        a = __builtin_fmaxf(a, __shfl_xor(a, 16, 64));
-        a = __builtin_fmaxf(a, __shfl_xor(a, 32, 64));
+        a = max_over_rows(a);
         if (g == 0) amx[wave * 64 + t * 16 + r16] = a;
       }
       __syncthreads();
@@ -715,8 +714,7 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
         float amax = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+        amax = max_over_rows(amax);
         const int E = block_scale_exp(amax);
         if (m < nrows) {
 #pragma unroll
@@ -922,8 +920,7 @@ __device__ void wave_tile(const KParams& p, const Shared& sh, const int* lr2s, b
         float amax = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
-        amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+        amax = max_over_rows(amax);
         const int E = block_scale_exp(amax);
         if (m < nrows) {
 #pragma unroll
@@ -1234,8 +1231,7 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
       float amax = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+      amax = max_over_rows(amax);
       const int E = block_scale_exp(amax);
 #pragma unroll
       for (int hh = 0; hh < 2; hh++)
@@ -1501,8 +1497,7 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
       float amax = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16, 64));
-      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32, 64));
+      amax = max_over_rows(amax);
       const int E = block_scale_exp(amax);
       if (m < nrows) {
         const size_t row = (size_t)(row0 + m);

@@ -1,6 +1,7 @@
-// Test helper: the forward's hardware pack conversions (e4m3x4 and bf16x2 of
-// the device helpers) applied to a list of floats, so that a test can compare
-// them with the oracle's encoders value by value.
+// Test helpers: the forward's device helpers applied to lists of floats, so
+// that tests can compare them value by value: the hardware pack conversions
+// (e4m3x4, bf16x2) with the oracle's encoders, and the cross-row lane maximum
+// (max_over_rows) with its definition.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -16,6 +17,11 @@ __global__ __launch_bounds__(256) void convert(const float* __restrict__ in, uin
 __global__ __launch_bounds__(256) void convert_bf16(const float* __restrict__ in, uint32_t* __restrict__ out, int npairs) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < npairs) out[i] = moeffn::bf16x2(in[2 * i], in[2 * i + 1]);
+}
+
+__global__ __launch_bounds__(256) void lane_max(const float* __restrict__ in, float* __restrict__ out, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;  // n is a multiple of 256: every lane of a wave is live
+  out[i] = moeffn::max_over_rows(in[i]);
 }
 
 }  // namespace
@@ -34,5 +40,13 @@ extern "C" int moe_test_bf16x2(const float* in, uint32_t* out, int npairs, void*
   if (npairs <= 0) return 0;
   hipLaunchKernelGGL(convert_bf16, dim3((npairs + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), in,
                      out, npairs);
+  return (int)hipGetLastError();
+}
+
+// in, out: n floats (device), n a positive multiple of 256; out[i] = max over lanes i^16, i^32, i^48 and i
+// of its 64-lane wave.
+extern "C" int moe_test_max_over_rows(const float* in, float* out, int n, void* stream) {
+  if (n <= 0 || n % 256) return 1;
+  hipLaunchKernelGGL(lane_max, dim3(n / 256), dim3(256), 0, static_cast<hipStream_t>(stream), in, out, n);
   return (int)hipGetLastError();
 }

@@ -1,4 +1,4 @@
-"""The forward's hardware pack conversions against the oracle's encoders (MI355X only).
+"""The forward's device helpers against the oracle's encoders and their definitions (MI355X only).
 
 The L1 epilogues and the pre-dispatch quantiser write their e4m3 codes with
 the hardware pack conversion (`e4m3x4` in the device helpers).  Its codes
@@ -13,7 +13,11 @@ The L2 epilogues round each slot's result to bf16 with the other pack
 conversion (`bf16x2`): its bits must be the oracle's round-to-nearest-even
 bf16 for every bf16 value, every midpoint between neighbours and the floats
 next to it, fp32 denormals and random finite values below 2^127 (the
-results are far from overflow; NaN is not an input)."""
+results are far from overflow; NaN is not an input).
+
+The L1 epilogues take each 1x32 block's largest magnitude over the four
+16-lane rows of a wave with the gfx950 lane-swap moves (`max_over_rows`):
+every lane must get the largest of lanes l, l^16, l^32 and l^48."""
 import ctypes
 import os
 
@@ -46,7 +50,7 @@ def conversion_inputs() -> np.ndarray:
 
 
 def test_e4m3x4_matches_oracle_encoder():
-    path = os.path.join(HERE, "native", "libmoe_convert.so")
+    path = os.path.join(HERE, "native", "libmoe_helpers.so")
     if not os.path.exists(path):
         pytest.fail(f"{path} is missing: build it with mixture_experts_ffn_histogram_amd/build.py build_test_helpers()")
     lib = ctypes.CDLL(path)
@@ -83,7 +87,7 @@ def bf16_inputs() -> np.ndarray:
 
 
 def test_bf16x2_matches_oracle_rounding():
-    path = os.path.join(HERE, "native", "libmoe_convert.so")
+    path = os.path.join(HERE, "native", "libmoe_helpers.so")
     if not os.path.exists(path):
         pytest.fail(f"{path} is missing: build it with mixture_experts_ffn_histogram_amd/build.py build_test_helpers()")
     lib = ctypes.CDLL(path)
@@ -101,3 +105,24 @@ def test_bf16x2_matches_oracle_rounding():
     bad = np.nonzero(got != ref)[0]
     assert bad.size == 0, (f"{bad.size} of {v.size} values differ, first: "
                            + ", ".join(f"{v[i]!r}: gpu 0x{got[i]:04x} oracle 0x{ref[i]:04x}" for i in bad[:6]))
+
+
+def test_max_over_rows_is_the_four_lane_max():
+    path = os.path.join(HERE, "native", "libmoe_helpers.so")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} is missing: build it with mixture_experts_ffn_histogram_amd/build.py build_test_helpers()")
+    lib = ctypes.CDLL(path)
+    lib.moe_test_max_over_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.moe_test_max_over_rows.restype = ctypes.c_int
+    rng = np.random.default_rng(9)
+    v = rng.normal(0.0, 10.0, 256 * 64).astype(np.float32)
+    v[::7] = np.abs(v[::7])                                   # ties and signs mixed
+    v[5::64] = v[5 ^ 16::64]
+    x = torch.from_numpy(v).cuda()
+    out = torch.zeros_like(x)
+    assert lib.moe_test_max_over_rows(x.data_ptr(), out.data_ptr(), v.size, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    w = v.reshape(-1, 64)
+    lanes = np.arange(64)
+    ref = np.maximum.reduce([w[:, lanes ^ d] for d in (0, 16, 32, 48)])
+    assert np.array_equal(out.cpu().numpy().reshape(-1, 64), ref)
