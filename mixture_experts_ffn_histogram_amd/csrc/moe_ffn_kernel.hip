@@ -12,7 +12,8 @@
 // Then, for every call:
 //   L1  tile queue of L1 tiles: gathered x rows x W1 on scaled MFMA, fused
 //       SwiGLU + clamp + 1x32 e8m0 re-quantisation -> h      -- grid barrier 2
-//   L2  tile queue of L2 tiles: h x W2 -> fp32 o per routed row -- grid barrier 3
+//   L2  tile queue of L2 tiles: h x W2 -> o per routed row (bf16; fp32 for the BF16
+//       recipe)                                               -- grid barrier 3
 //   C   combine: y[t] = sum over valid slots j (ascending) of w[t,j] o[row]
 //   X   the last workgroup out re-zeroes the control block.
 // The stages follow the method of the MegaMoE pages: dispatch (expert count,

@@ -244,7 +244,10 @@ static double dot(const double* a, const double* b, int64_t n) {
 /*   hq_out [I]  re-quantised activation value (optional)                    */
 /*   hq_codes [I] (e4m3 byte, or bf16 bits as uint16 when recipe is BF16),   */
 /*   hq_sf [I/32] e8m0 bytes (optional; FP8 recipes only)                    */
-/*   o_out  [H]  fp32 L2 output (required)                                   */
+/*   o_out  [H]  L2 output as fp32: bf16 values for the e4m3 recipes        */
+/*               (required)                                                  */
+/*   o_exact, o_eps [H]  exact L2 sums before that rounding and their      */
+/*               contraction-error bound (optional)                        */
 /* ------------------------------------------------------------------------ */
 /* Spacing of the E4M3 grid around |v| (v finite, |v| <= 448). */
 static double e4m3_spacing(double v) {
