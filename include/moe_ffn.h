@@ -156,8 +156,8 @@ int moe_ffn_forward(const moe_ffn_problem* problem, const moe_ffn_args* args,
    workspace the library keeps in a static device array of
    MOE_FFN_NOALLOC_MAX_WORKSPACE bytes per GPU (held until the process ends).
    Problems whose moe_ffn_get_workspace_size exceeds that return
-   MOE_FFN_ERR_WORKSPACE_TOO_SMALL (e.g. the DeepSeek shape up to about 256
-   tokens fits).  Each call clears the array's control block with a kernel on
+   MOE_FFN_ERR_WORKSPACE_TOO_SMALL (e.g. the DeepSeek shape up to 496 tokens
+   fits: 67.0 MB at 496, 67.5 MB at 500).  Each call clears the array's control block with a kernel on
    `stream` before the forward; calls that overlap on one GPU share the array
    and race.  Calls no hipMalloc / hipFree; other errors as moe_ffn_forward. */
 #define MOE_FFN_NOALLOC_MAX_WORKSPACE (64u << 20)
