@@ -62,26 +62,6 @@ __device__ __forceinline__ void buf_load_lds4(rsrc_t r, void* lds, uint32_t voff
 // Number formats
 // ---------------------------------------------------------------------------
 
-// fp32 -> OCP E4M3FN code, round to nearest even, saturating at +-448.
-// Normal range: round the fp32 mantissa to 3 bits on the integer pattern and
-// re-bias the exponent (127 -> 7).  Below 2^-6 the e4m3 grid is m * 2^-9, so
-// the code is rint(|q| * 512) (0..8; 8 is the smallest normal, code 0x08).
-__device__ __forceinline__ uint32_t f32_to_e4m3(float q) {
-  const uint32_t u = __float_as_uint(q);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const float a = __builtin_fabsf(q);
-  uint32_t code;
-  if (a < 0x1p-6f) {
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    uint32_t b = __float_as_uint(a);
-    b += 0x7FFFFu + ((b >> 20) & 1u);
-    code = (b >> 20) - (120u << 3);
-    code = code > 0x7Eu ? 0x7Eu : code;
-  }
-  return sign | code;
-}
-
 // fp32 -> bf16 bits, round to nearest even (overflow gives inf, NaN stays NaN).
 __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -109,23 +89,23 @@ __device__ __forceinline__ float max_over_rows(float a) {
   return __builtin_fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
-// Exponent E of the e8m0 scale of a 1x32 block: the smallest integer with
-// amax <= 448 * 2^E (448 = 1.75 * 2^8), clamped to [-127, 127]; 0 for an
-// all-zero block.  Exact on the fp32 bit pattern: with amax = f * 2^p,
-// f in [1, 2), E = p - 8 when f <= 1.75, else p - 7.
-// Four values to e4m3 codes packed into a dword (byte j = value j) with the
-// hardware pack conversion (round to nearest even).  For values in [-464,
-// 464] it gives f32_to_e4m3's codes bit for bit, magnitudes above 448
-// saturating to 448 (checked on gfx950 over every code, every midpoint and its
-// neighbours, fp32 denormals, (448, 464] and 1M random values).  The block
-// scales keep every scaled value within 448 (the fp32-scale recipe's quotient
-// within an ulp of it).
+// Four values to OCP E4M3FN codes packed into a dword (byte j = value j)
+// with the hardware pack conversion: round to nearest even, and for values
+// in [-464, 464] magnitudes above 448 saturate to 448 (checked on gfx950
+// against the oracle's rounding and encoder over every code, every midpoint
+// and its neighbours, fp32 denormals, (448, 464] and random values).  The
+// block scales keep every scaled value within 448 (the fp32-scale recipe's
+// quotient within an ulp of it).
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);  // bytes 0, 1
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);       // bytes 2, 3
   return (uint32_t)w;
 }
 
+// Exponent E of the e8m0 scale of a 1x32 block: the smallest integer with
+// amax <= 448 * 2^E (448 = 1.75 * 2^8), clamped to [-127, 127]; 0 for an
+// all-zero block.  Exact on the fp32 bit pattern: with amax = f * 2^p,
+// f in [1, 2), E = p - 8 when f <= 1.75, else p - 7.
 __device__ __forceinline__ int block_scale_exp(float amax) {
   if (!(amax > 0.0f)) return 0;
   const uint32_t b = __float_as_uint(amax);
