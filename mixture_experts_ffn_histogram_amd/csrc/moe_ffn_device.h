@@ -82,11 +82,15 @@ __device__ __forceinline__ uint32_t bf16x2(float a, float b) {
 // same index of the four 16-lane rows) with the lane-swap moves of gfx950:
 // the 32-lane swap pairs each lane with lane l^32, the 16-lane swap with l^16.
 // VALU moves, not LDS permutes.
+// Maximum of two floats that are not NaN (the NaN-propagating maximum: no
+// quieting of its inputs, one instruction).
+__device__ __forceinline__ float fmax_nn(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float max_over_rows(float a) {
   const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  a = __builtin_fmaxf(__uint_as_float(h[0]), __uint_as_float(h[1]));
+  a = fmax_nn(__uint_as_float(h[0]), __uint_as_float(h[1]));
   const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(a), false, false);
-  return __builtin_fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  return fmax_nn(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 // Four values to OCP E4M3FN codes packed into a dword (byte j = value j)
@@ -107,21 +111,22 @@ __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
 // all-zero block.  Exact on the fp32 bit pattern: with amax = f * 2^p,
 // f in [1, 2), E = p - 8 when f <= 1.75, else p - 7.
 __device__ __forceinline__ int block_scale_exp(float amax) {
-  if (!(amax > 0.0f)) return 0;
   const uint32_t b = __float_as_uint(amax);
-  const int ef = (int)(b >> 23);
-  int E = (ef == 0) ? -127 : (ef - 127) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
-  E = E < -127 ? -127 : E;
-  E = E > 127 ? 127 : E;
-  return E;
+  const int ef = (int)(b >> 23);  // 0 for a subnormal amax: E below -127, clamped
+  const int E = (ef - 127) - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0);
+  // at most 255 - 135 + 1 = 121 (infinite amax): no upper clamp; selected, not branched on
+  return amax > 0.0f ? (E < -127 ? -127 : E) : 0;
 }
 
-// SwiGLU of one (gate, up) pair with the optional symmetric clamp of both.
-__device__ __forceinline__ float swiglu(float g, float u, bool clamp_on, float c) {
-  if (clamp_on) {
-    g = __builtin_fminf(__builtin_fmaxf(g, -c), c);
-    u = __builtin_fminf(__builtin_fmaxf(u, -c), c);
-  }
+// The clamp bound of a call: c, or +infinity with the clamp off, so that the
+// clamp is one median-of-three per value and no branch (equal to the clamped
+// or unclamped value for every input but NaN).
+__device__ __forceinline__ float clamp_bound(bool clamp_on, float c) { return clamp_on ? c : __builtin_inff(); }
+
+// SwiGLU of one (gate, up) pair, both clamped to [-cb, cb] (cb from clamp_bound).
+__device__ __forceinline__ float swiglu(float g, float u, float cb) {
+  g = __builtin_amdgcn_fmed3f(g, -cb, cb);
+  u = __builtin_amdgcn_fmed3f(u, -cb, cb);
   const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
   return g * sig * u;
 }

@@ -664,7 +664,7 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
         for (int hh = 0; hh < 2; hh++)
 #pragma unroll
           for (int j = 0; j < 4; j++)
-            a = __builtin_fmaxf(a, __builtin_fabsf(swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp)));
+            a = fmax_nn(a, __builtin_fabsf(swiglu(acc[hh][t][j], acc[2 + hh][t][j], clamp_bound(p.clamp_on, p.clamp))));
         a = max_over_rows(a);
         if (g == 0) amx[wave * 64 + t * 16 + r16] = a;
       }
@@ -681,7 +681,7 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
           for (int hh = 0; hh < 2; hh++) {
             float q[4];
 #pragma unroll
-            for (int j = 0; j < 4; j++) q[j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp) / sc;
+            for (int j = 0; j < 4; j++) q[j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], clamp_bound(p.clamp_on, p.clamp)) / sc;
             stg4(p.h + row * I + (size_t)(i0 + hh * 16 + 4 * g), e4m3x4(q[0], q[1], q[2], q[3]));
           }
           if (wave == 0 && g == 0) stg4(p.h_sf + row * (size_t)(I / 32) + (size_t)nb * 4, __float_as_uint(sc));
@@ -700,7 +700,7 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
 #pragma unroll
       for (int hh = 0; hh < 2; hh++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp);
+        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], clamp_bound(p.clamp_on, p.clamp));
       const size_t row = (size_t)(row0 + m);
       if constexpr (C::kBF16) {
         if (m < nrows) {
@@ -714,7 +714,7 @@ __device__ void gemm_tile(const KParams& p, Shared& sh, SharedB<BM>& sb, const i
       } else {
         float amax = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
+        for (int j = 0; j < 8; j++) amax = fmax_nn(amax, __builtin_fabsf(hv[j]));
         amax = max_over_rows(amax);
         const int E = block_scale_exp(amax);
         if (m < nrows) {
@@ -906,7 +906,7 @@ __device__ void wave_tile(const KParams& p, const Shared& sh, const int* lr2s, b
 #pragma unroll
       for (int hh = 0; hh < 2; hh++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp);
+        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], clamp_bound(p.clamp_on, p.clamp));
       const size_t row = (size_t)(row0 + m);
       if constexpr (C::kBF16) {
         if (m < nrows) {
@@ -920,7 +920,7 @@ __device__ void wave_tile(const KParams& p, const Shared& sh, const int* lr2s, b
       } else {
         float amax = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
+        for (int j = 0; j < 8; j++) amax = fmax_nn(amax, __builtin_fabsf(hv[j]));
         amax = max_over_rows(amax);
         const int E = block_scale_exp(amax);
         if (m < nrows) {
@@ -1211,6 +1211,13 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   big_kloop<NT>(R.b0, R.b1, R.b2, acc, rW, a_off, a_soff, rWs, as_full, as_last, sa_base, rX, xoff, brd0, brd1,
                 rXs, xs_off, (uint32_t)p.sg_rows * 4u, nk, wave, lane);
 
+  // The epilogues' lane indices, taken anew after the K loop: derived from
+  // the thread index, their per-lane addresses would be hoisted out of the
+  // tile loop and held in registers through the K loop.
+  int tide = tid;
+  asm volatile("" : "+v"(tide));
+  const int lanee = tide & 63, ge = lanee >> 4, r16e = lanee & 15;
+
   if (l1) {
     // h through LDS (the ring buffers are free: the K loop ends on a
     // barrier): the tile's 128 rows x 128 code bytes go to buffer 0 (row
@@ -1221,37 +1228,38 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
     constexpr int kHStride = 144;
     uint8_t* hb = R.b0;
     uint8_t* sfb = R.b1;
+    const float cb = clamp_bound(p.clamp_on, p.clamp);
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      const int m = t * 16 + r16;
+      const int m = t * 16 + r16e;
       float hv[8];
 #pragma unroll
       for (int hh = 0; hh < 2; hh++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp);
+        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], cb);
       float amax = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
+      for (int j = 0; j < 8; j++) amax = fmax_nn(amax, __builtin_fabsf(hv[j]));
       amax = max_over_rows(amax);
       const int E = block_scale_exp(amax);
 #pragma unroll
       for (int hh = 0; hh < 2; hh++)
-        *(uint32_t*)(hb + m * kHStride + wave * 32 + hh * 16 + 4 * g) =
+        *(uint32_t*)(hb + m * kHStride + wave * 32 + hh * 16 + 4 * ge) =
             e4m3x4(__builtin_amdgcn_ldexpf(hv[hh * 4 + 0], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 1], -E),
                    __builtin_amdgcn_ldexpf(hv[hh * 4 + 2], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 3], -E));
-      if (g == 0) sfb[m * 4 + wave] = (uint8_t)(E + 127);
+      if (ge == 0) sfb[m * 4 + wave] = (uint8_t)(E + 127);
     }
     __syncthreads();
 #pragma unroll 1
     for (int k = 0; k < 4; k++) {  // 1024 pieces of 16 bytes: row piece / 8, chunk piece % 8
-      const int piece = k * kThreads + tid, r = piece >> 3, c = piece & 7;
+      const int piece = k * kThreads + tide, r = piece >> 3, c = piece & 7;
       if (r < nrows)
         stg16(p.h + (size_t)(row0 + r) * I + (size_t)(nb * 128 + c * 16), *(const v4i*)(hb + r * kHStride + c * 16));
     }
-    if (tid < nrows) {
-      const uint32_t sw = *(const uint32_t*)(sfb + tid * 4);
-      stg4(p.h_sf + (size_t)(row0 + tid) * (size_t)(I / 32) + (size_t)nb * 4, sw);
-      stg4(p.hsg + (size_t)nb * p.sg_rows + (size_t)(row0 + tid), sw);
+    if (tide < nrows) {
+      const uint32_t sw = *(const uint32_t*)(sfb + tide * 4);
+      stg4(p.h_sf + (size_t)(row0 + tide) * (size_t)(I / 32) + (size_t)nb * 4, sw);
+      stg4(p.hsg + (size_t)nb * p.sg_rows + (size_t)(row0 + tide), sw);
     }
   } else {
     // o through LDS, two 16-row blocks at a time (the ring buffers are free:
@@ -1265,7 +1273,7 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
     // but store the other waves' outputs.
     constexpr int kOStride = 528;
     static_assert(32 * kOStride <= kBigBuf, "a pair of 16-row blocks of o fits a ring buffer");
-    const int col = (lane & 31) * 8;  // this lane's 8 outputs of the tile's 256
+    const int col = (lanee & 31) * 8;  // this lane's 8 outputs of the tile's 256
 #pragma unroll
     for (int tp = 0; tp < NT / 2; tp++) {
       uint8_t* bp = tp % 3 == 0 ? R.b0 : tp % 3 == 1 ? R.b1 : R.b2;
@@ -1275,14 +1283,14 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
 #pragma unroll
           for (int j = 0; j < 4; j++) {
             const v4f& a = acc[j][2 * tp + hb];
-            *(uint2*)(bp + (hb * 16 + r16) * kOStride + (wave * 64 + 16 * j + 4 * g) * 2) =
+            *(uint2*)(bp + (hb * 16 + r16e) * kOStride + (wave * 64 + 16 * j + 4 * ge) * 2) =
                 uint2{bf16x2(a[0], a[1]), bf16x2(a[2], a[3])};
           }
       }
       __syncthreads();
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
-        const int lr = wave * 8 + rr * 2 + (lane >> 5);  // row of the pair
+        const int lr = wave * 8 + rr * 2 + (lanee >> 5);  // row of the pair
         const int m = tp * 32 + lr;
         const v4i v = *(const v4i*)(bp + lr * kOStride + col * 2);
         if (m < nrows && nb * 256 + col < H) stg16((uint16_t*)p.o + (size_t)(row0 + m) * H + (size_t)(nb * 256 + col), v);
@@ -1494,10 +1502,10 @@ __device__ void wave_tile_w4(const KParams& p, const Shared& sh, const int* lr2s
 #pragma unroll
       for (int hh = 0; hh < 2; hh++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], p.clamp_on, p.clamp);
+        for (int j = 0; j < 4; j++) hv[hh * 4 + j] = swiglu(acc[hh][t][j], acc[2 + hh][t][j], clamp_bound(p.clamp_on, p.clamp));
       float amax = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; j++) amax = __builtin_fmaxf(amax, __builtin_fabsf(hv[j]));
+      for (int j = 0; j < 8; j++) amax = fmax_nn(amax, __builtin_fabsf(hv[j]));
       amax = max_over_rows(amax);
       const int E = block_scale_exp(amax);
       if (m < nrows) {
