@@ -171,8 +171,8 @@ int moe_ffn_forward_noalloc(const moe_ffn_problem* problem, const moe_ffn_args* 
      dst[e*rows*k_blocks + (b*nk + 4G)*64 + i*4*n + u*4 + c] = src[e][r][4s + c],
      n = min(4, nk - 4G) (the stages in group G),
    i.e. per 16-row block, groups of four K stages, each group [16 rows][n
-   stages][4 blocks]: one 16-byte load brings a row's scales for four stages,
-   one 64-byte run a stage's scales for 16 rows.  src and dst: device buffers
+   stages][4 blocks]: one 16-byte load brings a row's scales for four stages;
+   a stage's scales of the 16 rows lie 4n bytes apart.  src and dst: device buffers
    of num_experts*rows*k_blocks bytes, 4-byte aligned, not overlapping.
    Enqueued on `stream` (a hipStream_t; NULL = default stream); asynchronous,
    allocates nothing.  Returns MOE_FFN_ERR_INVALID_ARG for null or misaligned

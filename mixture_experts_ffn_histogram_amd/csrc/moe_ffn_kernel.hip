@@ -1029,8 +1029,8 @@ __device__ __forceinline__ void big_kloop(uint8_t* __restrict__ B0, uint8_t* __r
   // beyond the first copy load zeros from past the end of the buffer into
   // further copies, so every wave issues the same count) and the scales of
   // the wave's own 64 weight rows from the TILED layout: lane l fetches the
-  // stage's dword (4 blocks) of row l%16 of its row block l/16 (a 64-byte run
-  // per block), stored as [wave][block j][row][4 bytes].
+  // stage's dword (4 blocks) of row l%16 of its row block l/16 (the 16 rows'
+  // dwords of a full group 16 bytes apart), stored as [wave][block j][row][4 bytes].
   auto dma = [&](int s, int buf) {
     uint8_t* bp = BUF(buf);
     const bool live = s < nk;
