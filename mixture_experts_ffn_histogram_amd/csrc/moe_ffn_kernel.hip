@@ -1214,9 +1214,9 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
   // The epilogues' lane indices, taken anew after the K loop: derived from
   // the thread index, their per-lane addresses would be hoisted out of the
   // tile loop and held in registers through the K loop.
-  int tide = tid;
-  asm volatile("" : "+v"(tide));
-  const int lanee = tide & 63, ge = lanee >> 4, r16e = lanee & 15;
+  int ep_tid = tid;
+  asm volatile("" : "+v"(ep_tid));
+  const int ep_lane = ep_tid & 63, ep_g = ep_lane >> 4, ep_r16 = ep_lane & 15;
 
   if (l1) {
     // h through LDS (the ring buffers are free: the K loop ends on a
@@ -1231,7 +1231,7 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
     const float cb = clamp_bound(p.clamp_on, p.clamp);
 #pragma unroll
     for (int t = 0; t < NT; t++) {
-      const int m = t * 16 + r16e;
+      const int m = t * 16 + ep_r16;
       float hv[8];
 #pragma unroll
       for (int hh = 0; hh < 2; hh++)
@@ -1244,22 +1244,22 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
       const int E = block_scale_exp(amax);
 #pragma unroll
       for (int hh = 0; hh < 2; hh++)
-        *(uint32_t*)(hb + m * kHStride + wave * 32 + hh * 16 + 4 * ge) =
+        *(uint32_t*)(hb + m * kHStride + wave * 32 + hh * 16 + 4 * ep_g) =
             e4m3x4(__builtin_amdgcn_ldexpf(hv[hh * 4 + 0], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 1], -E),
                    __builtin_amdgcn_ldexpf(hv[hh * 4 + 2], -E), __builtin_amdgcn_ldexpf(hv[hh * 4 + 3], -E));
-      if (ge == 0) sfb[m * 4 + wave] = (uint8_t)(E + 127);
+      if (ep_g == 0) sfb[m * 4 + wave] = (uint8_t)(E + 127);
     }
     __syncthreads();
 #pragma unroll 1
     for (int k = 0; k < 4; k++) {  // 1024 pieces of 16 bytes: row piece / 8, chunk piece % 8
-      const int piece = k * kThreads + tide, r = piece >> 3, c = piece & 7;
+      const int piece = k * kThreads + ep_tid, r = piece >> 3, c = piece & 7;
       if (r < nrows)
         stg16(p.h + (size_t)(row0 + r) * I + (size_t)(nb * 128 + c * 16), *(const v4i*)(hb + r * kHStride + c * 16));
     }
-    if (tide < nrows) {
-      const uint32_t sw = *(const uint32_t*)(sfb + tide * 4);
-      stg4(p.h_sf + (size_t)(row0 + tide) * (size_t)(I / 32) + (size_t)nb * 4, sw);
-      stg4(p.hsg + (size_t)nb * p.sg_rows + (size_t)(row0 + tide), sw);
+    if (ep_tid < nrows) {
+      const uint32_t sw = *(const uint32_t*)(sfb + ep_tid * 4);
+      stg4(p.h_sf + (size_t)(row0 + ep_tid) * (size_t)(I / 32) + (size_t)nb * 4, sw);
+      stg4(p.hsg + (size_t)nb * p.sg_rows + (size_t)(row0 + ep_tid), sw);
     }
   } else {
     // o through LDS, two 16-row blocks at a time (the ring buffers are free:
@@ -1273,7 +1273,7 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
     // but store the other waves' outputs.
     constexpr int kOStride = 528;
     static_assert(32 * kOStride <= kBigBuf, "a pair of 16-row blocks of o fits a ring buffer");
-    const int col = (lanee & 31) * 8;  // this lane's 8 outputs of the tile's 256
+    const int col = (ep_lane & 31) * 8;  // this lane's 8 outputs of the tile's 256
 #pragma unroll
     for (int tp = 0; tp < NT / 2; tp++) {
       uint8_t* bp = tp % 3 == 0 ? R.b0 : tp % 3 == 1 ? R.b1 : R.b2;
@@ -1283,14 +1283,14 @@ __device__ __forceinline__ void big_tile(const KParams& p, const Shared& sh, con
 #pragma unroll
           for (int j = 0; j < 4; j++) {
             const v4f& a = acc[j][2 * tp + hb];
-            *(uint2*)(bp + (hb * 16 + r16e) * kOStride + (wave * 64 + 16 * j + 4 * ge) * 2) =
+            *(uint2*)(bp + (hb * 16 + ep_r16) * kOStride + (wave * 64 + 16 * j + 4 * ep_g) * 2) =
                 uint2{bf16x2(a[0], a[1]), bf16x2(a[2], a[3])};
           }
       }
       __syncthreads();
 #pragma unroll
       for (int rr = 0; rr < 4; rr++) {
-        const int lr = wave * 8 + rr * 2 + (lanee >> 5);  // row of the pair
+        const int lr = wave * 8 + rr * 2 + (ep_lane >> 5);  // row of the pair
         const int m = tp * 32 + lr;
         const v4i v = *(const v4i*)(bp + lr * kOStride + col * 2);
         if (m < nrows && nb * 256 + col < H) stg16((uint16_t*)p.o + (size_t)(row0 + m) * H + (size_t)(nb * 256 + col), v);
