@@ -47,7 +47,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
 
 def build_test_helpers(verbose: bool = False) -> list:
     """Compile the test-only helpers (tests/native) for gfx950: the side-stream
-    kernel and the e4m3 conversion check."""
+    kernel and the device-helper checks."""
     root = os.path.dirname(HERE)
     outs = []
     for src_name, lib_name in (("side_kernel.hip", "libmoe_side.so"), ("device_helpers.hip", "libmoe_helpers.so")):

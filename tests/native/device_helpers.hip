@@ -1,7 +1,8 @@
 // Test helpers: the forward's device helpers applied to lists of floats, so
 // that tests can compare them value by value: the hardware pack conversions
-// (e4m3x4, bf16x2) with the oracle's encoders, and the cross-row lane maximum
-// (max_over_rows) with its definition.
+// (e4m3x4, bf16x2) with the oracle's encoders, the cross-row lane maximum
+// (max_over_rows) with its definition, and the 1x32 block exponent
+// (block_scale_exp) with the oracle's scale rule.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -22,6 +23,11 @@ __global__ __launch_bounds__(256) void convert_bf16(const float* __restrict__ in
 __global__ __launch_bounds__(256) void lane_max(const float* __restrict__ in, float* __restrict__ out, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;  // n is a multiple of 256: every lane of a wave is live
   out[i] = moeffn::max_over_rows(in[i]);
+}
+
+__global__ __launch_bounds__(256) void scale_exp(const float* __restrict__ in, int* __restrict__ out, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = moeffn::block_scale_exp(in[i]);
 }
 
 }  // namespace
@@ -48,5 +54,13 @@ extern "C" int moe_test_bf16x2(const float* in, uint32_t* out, int npairs, void*
 extern "C" int moe_test_max_over_rows(const float* in, float* out, int n, void* stream) {
   if (n <= 0 || n % 256) return 1;
   hipLaunchKernelGGL(lane_max, dim3(n / 256), dim3(256), 0, static_cast<hipStream_t>(stream), in, out, n);
+  return (int)hipGetLastError();
+}
+
+// in: n floats (device), out: n ints (device), out[i] = the e8m0 exponent the epilogues take for a block
+// whose largest magnitude is in[i].
+extern "C" int moe_test_block_scale_exp(const float* in, int* out, int n, void* stream) {
+  if (n <= 0) return 0;
+  hipLaunchKernelGGL(scale_exp, dim3((n + 255) / 256), dim3(256), 0, static_cast<hipStream_t>(stream), in, out, n);
   return (int)hipGetLastError();
 }

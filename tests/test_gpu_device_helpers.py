@@ -17,7 +17,14 @@ results are far from overflow; NaN is not an input).
 
 The L1 epilogues take each 1x32 block's largest magnitude over the four
 16-lane rows of a wave with the gfx950 lane-swap moves (`max_over_rows`):
-every lane must get the largest of lanes l, l^16, l^32 and l^48."""
+every lane must get the largest of lanes l, l^16, l^32 and l^48.
+
+The block's e8m0 exponent (`block_scale_exp`, read off the fp32 bits with
+selects, no branches) must be the oracle's scale rule for every largest
+magnitude a block can have: zero, fp32 denormals, each boundary 448 * 2^E of
+the clamped range and the floats next to it, mantissas next to 1.75, the
+largest finite float, NaN (exponent 0), and random values over the range.
+(+infinity is outside: no block of finite products reaches it.)"""
 import ctypes
 import os
 
@@ -126,3 +133,36 @@ def test_max_over_rows_is_the_four_lane_max():
     lanes = np.arange(64)
     ref = np.maximum.reduce([w[:, lanes ^ d] for d in (0, 16, 32, 48)])
     assert np.array_equal(out.cpu().numpy().reshape(-1, 64), ref)
+
+
+def test_block_scale_exp_matches_oracle_rule():
+    path = os.path.join(HERE, "native", "libmoe_helpers.so")
+    if not os.path.exists(path):
+        pytest.fail(f"{path} is missing: build it with mixture_experts_ffn_histogram_amd/build.py build_test_helpers()")
+    lib = ctypes.CDLL(path)
+    lib.moe_test_block_scale_exp.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    lib.moe_test_block_scale_exp.restype = ctypes.c_int
+    f32 = np.float32
+    vals = [0.0, -0.0, float("nan"), float(np.finfo(f32).max), float(np.finfo(f32).tiny)]
+    vals += list(np.arange(1, 65, dtype=np.uint32).view(f32))                  # smallest denormals
+    vals += list((np.uint32(0x007FFFFF) - np.arange(64, dtype=np.uint32)).view(f32))  # largest denormals
+    for E in range(-140, 121):
+        b = f32(np.ldexp(448.0, E))                                              # 448 * 2^E (denormal below -133)
+        if b == 0 or not np.isfinite(b):
+            continue
+        vals += [float(b), float(np.nextafter(b, f32(0))), float(np.nextafter(b, f32(np.inf)))]
+    for p in range(-126, 127, 3):                                               # mantissas next to 1.75
+        m = f32(np.ldexp(1.75, p))
+        vals += [float(np.nextafter(m, f32(0))), float(m), float(np.nextafter(m, f32(np.inf)))]
+    rng = np.random.default_rng(77)
+    vals += list(np.exp2(rng.uniform(-149.0, 127.9, 50_000)).astype(f32))
+    v = np.asarray(vals, f32)
+    x = torch.from_numpy(v).cuda()
+    out = torch.zeros(v.size, dtype=torch.int32, device="cuda")
+    assert lib.moe_test_block_scale_exp(x.data_ptr(), out.data_ptr(), v.size, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = np.array([oracle.scale_exp(float(a)) for a in v], np.int32)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, (f"{bad.size} of {v.size} differ, first: "
+                           + ", ".join(f"{v[i]!r}: gpu {got[i]} oracle {ref[i]}" for i in bad[:6]))
