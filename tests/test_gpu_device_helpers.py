@@ -146,9 +146,9 @@ def test_block_scale_exp_matches_oracle_rule():
     vals = [0.0, -0.0, float("nan"), float(np.finfo(f32).max), float(np.finfo(f32).tiny)]
     vals += list(np.arange(1, 65, dtype=np.uint32).view(f32))                  # smallest denormals
     vals += list((np.uint32(0x007FFFFF) - np.arange(64, dtype=np.uint32)).view(f32))  # largest denormals
-    for E in range(-140, 121):
+    for E in range(-140, 120):                                                  # 448 * 2^119 is the last finite one
         b = f32(np.ldexp(448.0, E))                                              # 448 * 2^E (denormal below -133)
-        if b == 0 or not np.isfinite(b):
+        if b == 0:
             continue
         vals += [float(b), float(np.nextafter(b, f32(0))), float(np.nextafter(b, f32(np.inf)))]
     for p in range(-126, 127, 3):                                               # mantissas next to 1.75
